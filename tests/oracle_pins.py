@@ -1,0 +1,390 @@
+"""Pins of the CPU oracle: checks that tie it to something other than itself.
+
+Each check raises AssertionError on failure.  They are collected as tests in
+test_oracle_pins.py, and test_oracle_mutations.py plants plausible mistakes
+in the oracle (on the CPU) to show that some check here goes red for each.
+
+Sources of the expected values: the pages' own facts (the fills of gate 4 in
+TensorFold PR #1467, the byte counts of the span-restricted head in PR #1507),
+closed forms of the Hadamard transform and of the linear with constant
+weights, library routines for the IEEE conversions (numpy float16, torch
+bfloat16), brute force on tiny inputs written with plain Python bit strings,
+and the hand-worked codebook example under tests/golden/.
+"""
+
+from __future__ import annotations
+
+import os
+
+import numpy as np
+
+from oracle import exl3_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+# --------------------------------------------------------------- conversions
+
+def check_fp16_decode_all_patterns():
+    pats = np.arange(65536, dtype=np.uint16)
+    ours = O.fp16_to_f64(pats)
+    ref = pats.view(np.float16).astype(np.float64)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), nan)
+    assert np.array_equal(ours[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(ours[~nan]), np.signbit(ref[~nan]))
+
+
+def check_fp16_round_vs_numpy():
+    rng = np.random.default_rng(1234)
+    # wide exponent range, exact ties, subnormals, overflow boundary, specials
+    mant = rng.uniform(-1, 1, size=200000)
+    expo = rng.integers(-30, 18, size=mant.size)
+    x = np.ldexp(mant, expo)
+    grid = np.arange(-70000, 70000, 0.5) / 1.0
+    ties = np.ldexp(np.arange(1, 4097, dtype=np.float64) + 0.5, -11)          # halfway at exponent 0
+    sub_ties = np.ldexp(np.arange(0, 2048, dtype=np.float64) + 0.5, -24)      # halfway subnormals
+    edge = np.array([0.0, -0.0, 65504.0, 65519.99, 65520.0, 65536.0, -65520.0, 1e300, -1e300,
+                     np.ldexp(1.0, -25), np.ldexp(1.0, -26), np.ldexp(3.0, -26),
+                     np.inf, -np.inf, np.nan])
+    x = np.concatenate([x, grid, ties, -ties, sub_ties, -sub_ties, edge])
+    ours = O.f64_to_fp16(x)
+    ref = x.astype(np.float16).view(np.uint16)
+    nan = np.isnan(x)
+    assert np.array_equal(ours[~nan], ref[~nan]), np.flatnonzero(ours[~nan] != ref[~nan])[:10]
+    assert np.all((ours[nan] & 0x7C00) == 0x7C00) and np.all((ours[nan] & 0x3FF) != 0)
+
+
+def check_bf16_decode_all_patterns():
+    import torch
+    pats = np.arange(65536, dtype=np.uint16)
+    ours = O.bf16_to_f64(pats)
+    ref = torch.from_numpy(pats.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), nan)
+    assert np.array_equal(ours[~nan], ref[~nan])
+
+
+def check_bf16_round_vs_torch():
+    import torch
+    rng = np.random.default_rng(99)
+    mant = rng.uniform(-1, 1, size=200000).astype(np.float32)
+    expo = rng.integers(-140, 128, size=mant.size)
+    x32 = np.ldexp(mant, expo).astype(np.float32)
+    ties = (np.ldexp(np.arange(1, 257, dtype=np.float64) + 0.5, -7)).astype(np.float32)
+    edge = np.array([0.0, -0.0, 3.3895314e38, 3.4e38, np.finfo(np.float32).max, 1e-40, -1e-45,
+                     np.inf, -np.inf], dtype=np.float32)
+    x32 = np.concatenate([x32, ties, -ties, edge])
+    ours = O.f64_to_bf16(x32.astype(np.float64))
+    ref = torch.from_numpy(x32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, ref), np.flatnonzero(ours != ref)[:10]
+
+
+# ------------------------------------------------------------------ codebook
+
+def load_codebook_golden():
+    rows = []
+    with open(os.path.join(GOLDEN, "codebook_worked_example.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            s, t, b, v = line.split()
+            rows.append((int(s, 16), int(t, 16), int(b, 16), float(v)))
+    return rows
+
+
+def check_codebook_worked_example():
+    for s, _t, b, v in load_codebook_golden():
+        got = int(O.codebook(np.array([s]))[0])
+        assert got == b, (hex(s), hex(got), hex(b))
+        assert O.fp16_to_f64(np.array([got]))[0] == v
+
+
+def check_codebook_structure():
+    cb = O.codebook(np.arange(65536))
+    v = O.fp16_to_f64(cb)
+    # every weight finite, in +-[1/8, 2)
+    assert np.all(np.isfinite(v)) and np.all(np.abs(v) >= 0.125) and np.all(np.abs(v) < 2.0)
+    # the affine map is a bijection of the states and the mask drops three
+    # exponent bits: 8192 distinct weights, each reached by exactly 8 states
+    _, counts = np.unique(cb, return_counts=True)
+    assert counts.size == 8192 and np.all(counts == 8)
+    # exactly half negative and a symmetric value multiset (mean exactly 0)
+    assert (v < 0).sum() == 32768 and v.sum() == 0.0
+    # flipping the state's top bit adds 2^15 to t (odd multiplier), so it
+    # flips the sign bit of the weight and nothing else
+    s = np.arange(65536)
+    assert np.array_equal(O.codebook(s ^ 0x8000), cb ^ 0x8000)
+
+
+# -------------------------------------------------------------- trellis decode
+
+def _bitstring(tile_bytes):
+    """Stream bits of one tile as a Python string, bit j = bit j%8 of byte j//8."""
+    return "".join(format(int(byte), "08b")[::-1] for byte in tile_bytes)
+
+
+def _states_by_strings(tile_bytes, bits):
+    s = _bitstring(tile_bytes)
+    L = len(s)
+    out = []
+    for i in range(256):
+        w = "".join(s[(i * bits + t) % L] for t in range(16))    # LSB first
+        out.append(int(w[::-1], 2))
+    return out
+
+
+def check_windows_single_bit():
+    """A stream with one set bit p: exactly the weights whose window covers p
+    see it, at window position (p - i*b) mod 256b.  Pins the LSB-first order,
+    the window start i*b and the tail-biting wrap."""
+    for bits in (2, 3, 4, 5, 6, 8):
+        L = 256 * bits
+        for p in (0, 1, 7, 15, 16, L // 2 + 3, L - 9, L - 1):
+            tb = np.zeros(32 * bits, dtype=np.uint8)
+            tb[p // 8] = 1 << (p % 8)
+            st = O.tile_states(tb, bits)
+            for i in range(256):
+                d = (p - i * bits) % L
+                expect = (1 << d) if d < 16 else 0
+                assert int(st[i]) == expect, (bits, p, i, int(st[i]), expect)
+
+
+def check_windows_random_vs_strings():
+    rng = np.random.default_rng(7)
+    for bits in (2, 3, 4, 5, 6, 7, 8):
+        tb = rng.integers(0, 256, size=32 * bits, dtype=np.uint8)
+        assert [int(v) for v in O.tile_states(tb, bits)] == _states_by_strings(tb, bits)
+
+
+def check_fills_from_the_pages():
+    """TensorFold PR #1467 (gate 4): all-ones states decode to one weight at
+    every width; a 0xaaaa fill decodes to two alternating weights at 3 and 5
+    bits because their windows start at odd offsets (and to one weight at even
+    widths)."""
+    for bits in range(2, 9):
+        n = 32 * bits
+        ones = O.codebook(O.tile_states(np.full(n, 0xFF, np.uint8), bits))
+        assert np.unique(ones).size == 1
+        zeros = O.codebook(O.tile_states(np.zeros(n, np.uint8), bits))
+        assert np.unique(zeros).size == 1
+        aa = O.codebook(O.tile_states(np.full(n, 0xAA, np.uint8), bits))
+        if bits % 2 == 1:
+            assert np.unique(aa).size == 2
+            assert np.all(aa[0::2] == aa[0]) and np.all(aa[1::2] == aa[1]) and aa[0] != aa[1]
+            # even windows start at even offsets: state 0xAAAA; odd ones 0x5555
+            assert aa[0] == O.codebook(np.array([0xAAAA]))[0]
+            assert aa[1] == O.codebook(np.array([0x5555]))[0]
+        else:
+            assert np.unique(aa).size == 1
+
+
+def check_tile_placement():
+    """One set stream bit in a 256x256 weight (2 blocks): the changed weights
+    sit at K row 16kt + i%16 and column 128nb + 16t + i//16 of the tile that
+    holds the bit (tile order nb, kt, t; weight i walks down a column)."""
+    K = N = 256
+    for bits in (3, 4, 6):
+        tb = 32 * bits
+        base = O.decode(np.zeros(O.packed_bytes(K, N, bits), np.uint8), K, N, bits)
+        for byte_pos in (0, 5, tb - 1, tb + 3, 9 * tb + 1, 16 * 8 * tb + 2 * tb + 7, O.packed_bytes(K, N, bits) - 1):
+            words = np.zeros(O.packed_bytes(K, N, bits), np.uint8)
+            words[byte_pos] = 0x10
+            W = O.decode(words, K, N, bits)
+            tile_idx, in_tile = divmod(byte_pos, tb)
+            nb, rest = divmod(tile_idx, (K // 16) * 8)
+            kt, t = divmod(rest, 8)
+            p = in_tile * 8 + 4
+            want = set()
+            for i in range(256):
+                if (p - i * bits) % (256 * bits) < 16:
+                    want.add((16 * kt + i % 16, 128 * nb + 16 * t + i // 16))
+            got = set(zip(*np.nonzero(W != base)))
+            got = {(int(a), int(b)) for a, b in got}
+            # a changed state can map to the same weight only by a codebook
+            # collision (8 states per weight); require got to be inside want
+            # and to miss at most a few collisions
+            assert got <= want and len(want - got) <= 2, (bits, byte_pos, sorted(want - got)[:4], sorted(got - want)[:4])
+
+
+def check_view_decode_equals_parent_columns():
+    K, N, bits = 256, 512, 4
+    rng = np.random.default_rng(3)
+    words = rng.integers(0, 256, size=O.packed_bytes(K, N, bits), dtype=np.uint8)
+    W = O.decode(words, K, N, bits)
+    bs = O.block_bytes(K, bits)
+    for b0, nb in ((0, 1), (1, 2), (3, 1), (0, 4)):
+        Wv = O.decode(words, K, 128 * nb, bits, block_stride=bs, offset=b0 * bs)
+        assert np.array_equal(Wv, W[:, 128 * b0:128 * (b0 + nb)])
+
+
+def check_head_byte_accounting():
+    """TensorFold PR #1507: the 6-bit head 5120 -> 248,320 skips "~545 MB" when
+    only the two span views are read, and a 64-block tail reads "about 30 MB
+    more" than a 384-column (3-block) tail; the first span is 39.7 % of the
+    vocabulary with the 288 kept tail columns.  Storage is exactly 6 bits per
+    weight, so a block is 5120*128*6/8 bytes."""
+    K, bits = 5120, 6
+    blk = O.block_bytes(K, bits)
+    assert blk == K * 128 * bits // 8
+    head = O.packed_bytes(K, 248320, bits)
+    assert head == 1940 * blk == 953548800
+    spans = (768 + 64) * blk
+    assert round((head - spans) / 1e6) == 545
+    assert round((64 - 3) * blk / 1e6) == 30
+    assert round(100 * (98304 + 288) / 248320, 1) == 39.7
+    assert 248032 - 240128 == 7904 and 240128 + 64 * 128 == 248320
+
+
+# ------------------------------------------------------------------ Hadamard
+
+def _hadamard_closed_form(n=128):
+    i = np.arange(n)
+    pc = np.vectorize(lambda v: bin(int(v)).count("1"))(i[:, None] & i[None, :])
+    return np.where(pc % 2 == 0, 1.0, -1.0)
+
+
+def check_fwht_closed_form():
+    H = _hadamard_closed_form()
+    E = np.eye(128)
+    got = O.fwht128(E)                       # row j = FWHT(e_j) = e_j . H
+    assert np.array_equal(got, H)
+    assert np.array_equal(H @ H.T, 128 * np.eye(128))
+    rng = np.random.default_rng(5)
+    v = rng.standard_normal((4, 256))
+    assert np.allclose(O.fwht128(O.fwht128(v)), 128 * v, rtol=0, atol=1e-12)
+    # Parseval: ||v H||^2 = 128 ||v||^2
+    assert np.allclose((O.fwht128(v) ** 2).sum(axis=1), 128 * (v ** 2).sum(axis=1))
+
+
+def check_rot_in_one_hot():
+    """X = a one-hot row at column 128c + j: the rotated row is
+    fp16(a * suh[128c+j] * H[j, :] / 16) on chunk c and zero elsewhere."""
+    H = _hadamard_closed_form()
+    K = 384
+    rng = np.random.default_rng(11)
+    suh = np.where(rng.integers(0, 2, K) == 1, 0xBC00, 0x3C00).astype(np.uint16)
+    for col in (0, 5, 127, 128 + 77, 383):
+        for a, abits in ((1.0, 0x3F80), (-3.0, 0xC040), (0.15625, 0x3E20)):
+            x = np.zeros((1, K), np.uint16)
+            x[0, col] = abits
+            xr = O.fp16_to_f64(O.rot_in(x, suh))[0]
+            c, j = divmod(col, 128)
+            s = -1.0 if suh[col] == 0xBC00 else 1.0
+            expect = np.zeros(K)
+            expect[128 * c:128 * (c + 1)] = a * s * H[j, :] / 16
+            assert np.array_equal(xr, expect)
+
+
+# --------------------------------------------------------------- the linear
+
+def _blockdiag_h(n):
+    H = _hadamard_closed_form()
+    out = np.zeros((n, n))
+    for b in range(n // 128):
+        out[128 * b:128 * (b + 1), 128 * b:128 * (b + 1)] = H
+    return out
+
+
+def check_dense_brute_force():
+    """Dense check on the tiny configuration (K = N = 256, 4 bits, M = 1, 3,
+    16): materialise W_full = D_suh (Hb/16) (W D_scale) (Hb/8) D_svh in float64
+    from the closed-form Hadamard and compare X . W_full with the oracle's
+    unrounded result."""
+    from trellis_quantized_linear_amd import synth
+    K = N = 256
+    L = synth.gen_layer("tiny", "w", K, N, 4)
+    W = O.fp16_to_f64(O.decode(L.words, K, N, 4))
+    Hb = _blockdiag_h(K)
+    Wfull = (np.diag(O.fp16_to_f64(L.suh)) @ (Hb / 16) @ (W * O.fp16_to_f64(L.scales)[None, :])
+             @ (_blockdiag_h(N) / 8) @ np.diag(O.fp16_to_f64(L.svh)))
+    for M in (1, 3, 16):
+        x = synth.gen_x(synth.rng_for("tiny", "x", M), M, K)
+        ref = O.bf16_to_f64(x) @ Wfull
+        got = O.linear_packed(L.words, K, N, 4, L.scales, L.suh, L.svh, x, exact=True)
+        assert np.allclose(got, ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
+        # the rounded result is the rounding of the exact one up to the fp16
+        # rounding of the rotated input: well inside 1e-2 of the largest output
+        y = O.bf16_to_f64(O.linear_packed(L.words, K, N, 4, L.scales, L.suh, L.svh, x))
+        assert np.max(np.abs(y - ref)) <= 1e-2 * np.abs(ref).max()
+
+
+def closed_form_constant(x_vals, suh_vals, svh_vals, c):
+    """All weights equal c and scales 1: Y[m, 128b] = 128 c svh[128b]
+    sum_j x[m, 128j] suh[128j]; every other column is zero."""
+    M, K = x_vals.shape
+    N = svh_vals.size
+    s = (x_vals[:, ::128] * suh_vals[None, ::128]).sum(axis=1)
+    Y = np.zeros((M, N))
+    Y[:, ::128] = 128 * c * s[:, None] * svh_vals[None, ::128]
+    return Y
+
+
+def check_constant_weight_closed_form():
+    rng = np.random.default_rng(21)
+    for bits in (3, 4, 6):
+        K, N, M = 512, 256, 5
+        words = np.full(O.packed_bytes(K, N, bits), 0xFF, np.uint8)   # all-ones states
+        c = O.fp16_to_f64(O.codebook(np.array([0xFFFF])))[0]
+        xv = rng.integers(-3, 4, size=(M, K)).astype(np.float64)
+        x = O.f64_to_bf16(xv)
+        suh = np.where(rng.integers(0, 2, K) == 1, 0xBC00, 0x3C00).astype(np.uint16)
+        svh = np.where(rng.integers(0, 2, N) == 1, 0xBC00, 0x3C00).astype(np.uint16)
+        ones = np.full(N, 0x3C00, np.uint16)
+        y = O.linear_packed(words, K, N, bits, ones, suh, svh, x, exact=True)
+        ref = closed_form_constant(xv, O.fp16_to_f64(suh), O.fp16_to_f64(svh), c)
+        assert np.allclose(y, ref, rtol=0, atol=1e-9)
+
+
+def check_fp32_stress_exceeds_fp16():
+    """PR #1467 gate 4: a constant weight times rotated inputs of 4096; the K
+    sums leave the fp16 range (65504) while the result stays finite.  With
+    x[m, 128j] = 2^16 and zero elsewhere every rotated input is 4096."""
+    K, N, bits = 5120, 128, 4
+    words = np.full(O.packed_bytes(K, N, bits), 0xFF, np.uint8)
+    xv = np.zeros((1, K))
+    xv[0, ::128] = 65536.0
+    ones_k = np.full(K, 0x3C00, np.uint16)
+    xr = O.fp16_to_f64(O.rot_in(O.f64_to_bf16(xv), ones_k))
+    assert np.all(xr == 4096.0)
+    c = O.fp16_to_f64(O.codebook(np.array([0xFFFF])))[0]
+    y = O.linear_packed(words, K, N, bits, np.full(N, 0x3C00, np.uint16), ones_k,
+                        np.full(N, 0x3C00, np.uint16), O.f64_to_bf16(xv), exact=True)
+    z = c * 4096.0 * K
+    assert abs(z) > 65504
+    assert y[0, 0] == 128 * c * 40 * 65536.0 and np.all(y[0, 1:] == 0)
+
+
+def check_special_values_propagate():
+    """PR #1467 gate 1: planted NaN and both infinities reach the outputs."""
+    from trellis_quantized_linear_amd import synth
+    K, N, bits, M = 256, 256, 4, 4
+    L = synth.gen_layer("special", "w", K, N, bits)
+    x = synth.gen_x(synth.rng_for("special", "x"), M, K)
+    x[0, 3] = 0x7FC0        # NaN
+    x[1, 200] = 0x7F80      # +Inf
+    x[2, 17] = 0xFF80       # -Inf
+    y = O.bf16_to_f64(O.linear_packed(L.words, K, N, bits, L.scales, L.suh, L.svh, x))
+    assert np.all(np.isnan(y[0]))
+    # one infinity spreads over its chunk by the rotation, then mixed-sign
+    # weights add +inf and -inf: every output of the row is NaN
+    assert np.all(np.isnan(y[1])) and np.all(np.isnan(y[2]))
+    assert np.all(np.isfinite(y[3]))
+    # an infinite scale poisons its own block only
+    sc = L.scales.copy()
+    sc[130] = 0x7C00
+    y2 = O.bf16_to_f64(O.linear_packed(L.words, K, N, bits, sc, L.suh, L.svh, x[3:4]))
+    assert np.all(~np.isfinite(y2[0, 128:])) and np.all(np.isfinite(y2[0, :128]))
+
+
+ALL_CHECKS = [
+    check_fp16_decode_all_patterns, check_fp16_round_vs_numpy,
+    check_bf16_decode_all_patterns, check_bf16_round_vs_torch,
+    check_codebook_worked_example, check_codebook_structure,
+    check_windows_single_bit, check_windows_random_vs_strings, check_fills_from_the_pages,
+    check_tile_placement, check_view_decode_equals_parent_columns, check_head_byte_accounting,
+    check_fwht_closed_form, check_rot_in_one_hot,
+    check_dense_brute_force, check_constant_weight_closed_form, check_fp32_stress_exceeds_fp16,
+    check_special_values_propagate,
+]
