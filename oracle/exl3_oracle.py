@@ -198,16 +198,17 @@ def decode(words, K: int, N: int, bits: int, block_stride: int | None = None,
         block_stride = block_bytes(K, bits)
     buf = np.asarray(words, dtype=np.uint8).reshape(-1)
     nblk, kts, tb = N // BLOCK_COLS, K // TILE, 32 * bits
-    starts = (offset + np.arange(nblk)[:, None, None] * block_stride
-              + (np.arange(kts)[None, :, None] * 8 + np.arange(8)[None, None, :]) * tb)
-    tiles = buf[starts[..., None] + np.arange(tb)]                   # [nblk, kts, 8, tb]
-    w_tiles = codebook(tile_states(tiles, bits))                      # [nblk, kts, 8, 256]
     i = np.arange(256)
+    rows = np.broadcast_to(np.arange(kts)[:, None, None] * TILE + (i % TILE)[None, None, :], (kts, 8, 256))
     W = np.empty((K, N), dtype=np.uint16)
-    rows = np.arange(kts)[:, None, None] * TILE + (i % TILE)[None, None, :]        # [kts,1,256]
-    for nb in range(nblk):
-        cols = nb * BLOCK_COLS + np.arange(8)[None, :, None] * TILE + (i // TILE)[None, None, :]
-        W[np.broadcast_to(rows, (kts, 8, 256)), np.broadcast_to(cols, (kts, 8, 256))] = w_tiles[nb]
+    for nb in range(nblk):                                   # one column block at a time
+        starts = (offset + nb * block_stride
+                  + (np.arange(kts)[:, None] * 8 + np.arange(8)[None, :]) * tb)      # [kts, 8]
+        tiles = buf[starts[..., None] + np.arange(tb)]                              # [kts, 8, tb]
+        w_tiles = codebook(tile_states(tiles, bits))                                 # [kts, 8, 256]
+        cols = np.broadcast_to(nb * BLOCK_COLS + np.arange(8)[None, :, None] * TILE
+                               + (i // TILE)[None, None, :], (kts, 8, 256))
+        W[rows, cols] = w_tiles
     return W
 
 

@@ -1,0 +1,230 @@
+"""GPU self-consistency, bitwise: a row's bytes do not depend on how many rows
+are in the call, on the row tiling or launch shape, on group membership or on
+column views (TensorFold PR #1467 "The arithmetic" and its gate 3; PR #1407
+review item 1; PR #1507 "the views plan as the whole head, so the logits keep
+their bits"). Counters are zero whenever no call runs (PR #1475).
+
+Planted controls (another K split, a member's scales swapped, a member's suh
+swapped) must change bytes, which shows the comparisons can see a change.
+"""
+
+import numpy as np
+import pytest
+
+import gpu_util as G
+from oracle import exl3_oracle as O
+from trellis_quantized_linear_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+def ex():
+    import trellis_quantized_linear_amd.exl3 as m
+    return m
+
+
+@pytest.fixture(autouse=True)
+def _hooks():
+    ex().lib()
+    ex().exl3_test_force(-1, -1, 0)
+    yield
+    ex().exl3_test_force(-1, -1, 0)
+
+
+# weights covering each plan kind: narrow (S=32 and S=8), wide (S=4), K=17408
+SHAPES = [("k", 5120, 1024, 4), ("q", 5120, 6144, 4), ("wide", 5120, 8192, 4), ("down", 17408, 5120, 4),
+          ("gate3", 5120, 2048, 3), ("head6", 5120, 8192, 6)]
+
+
+@pytest.mark.parametrize("name,K,N,bits", SHAPES)
+def test_rows_identical_for_every_row_count(name, K, N, bits):
+    L = G.layer("rows", name, K, N, bits)
+    w = G.upload(L)
+    x = G.xbits("rows", 128, K)
+    xd = G.dev_bf16(x)
+    full = G.host_u16(G.run(w, xd, M=128, tag=f"rows {name} M=128"))
+    for M in (1, 2, 7, 15, 16, 17, 24, 32, 33, 48, 49, 64, 100, 127):
+        y = G.host_u16(G.run(w, xd, M=M, tag=f"rows {name}"))
+        assert np.array_equal(y[:M], full[:M]), (name, M)
+
+
+@pytest.mark.parametrize("name,K,N,bits", SHAPES[:4])
+def test_rows_identical_for_every_tiling_and_launch_shape(name, K, N, bits):
+    """The min_rows analogue: force each row tiling (1, 2, 4, 8 MFMA row tiles
+    per workgroup) and each launch shape (one split per workgroup with counter
+    exchange, or every split in one workgroup) at several row counts."""
+    L = G.layer("tiling", name, K, N, bits)
+    w = G.upload(L)
+    x = G.xbits("tiling", 40, K)
+    xd = G.dev_bf16(x)
+    ref = G.host_u16(G.run(w, xd, M=40, tag="auto"))
+    for mt in (1, 2, 4, 8):
+        for chained in (0, 1):
+            ex().exl3_test_force(mt, chained, 0)
+            for M in (1, 16, 17, 40):
+                y = G.host_u16(G.run(w, xd, M=M, tag=f"forced m_tiles={mt} chained={chained}"))
+                assert np.array_equal(y[:M], ref[:M]), (name, mt, chained, M)
+    ex().exl3_test_force(-1, -1, 0)
+
+
+def test_prompt_rows_equal_decode_rows():
+    """A prompt of 300 rows (3 row blocks, ragged) against single-row calls."""
+    K, N = 5120, 6144
+    L = G.layer("prompt", "q", K, N, 4)
+    w = G.upload(L)
+    x = G.xbits("prompt", 300, K, sigma=0.5)
+    xd = G.dev_bf16(x)
+    full = G.host_u16(G.run(w, xd, M=300, tag="prompt 300"))
+    for r in (0, 1, 127, 128, 200, 255, 256, 299):
+        one = G.host_u16(G.run(w, xd[r:r + 1], M=1, tag=f"decode row {r}"))
+        assert np.array_equal(one[0], full[r]), r
+    # a 16-row window inside the prompt equals the same rows of the prompt
+    win = G.host_u16(G.run(w, xd[128:144], M=16, tag="window"))
+    assert np.array_equal(win, full[128:144])
+
+
+@pytest.mark.parametrize("M", [1, 7, 16])
+def test_group_equals_each_member_alone(M):
+    """PR #1467 exl3-midm: the q/k/v and gate/up groups equal each member's own
+    launch at 1, 7 and 16 rows."""
+    K = synth.HIDDEN
+    x = G.xbits("group", M, K)
+    xd = G.dev_bf16(x)
+    for names in (("q", "k", "v"), ("gate", "up")):
+        cols = {"q": synth.Q_COLS, "k": synth.KV_COLS, "v": synth.KV_COLS,
+                "gate": synth.INTERMEDIATE, "up": synth.INTERMEDIATE}
+        layers = [G.layer("group", n, K, cols[n], 4) for n in names]
+        ws_ = [G.upload(L) for L in layers]
+        ys = G.run_group(ws_, xd, tag="+".join(names))
+        for n, w, y in zip(names, ws_, ys):
+            solo = G.host_u16(G.run(w, xd, tag=f"solo {n}"))
+            assert np.array_equal(G.host_u16(y), solo), (names, n, M)
+
+
+def test_group_planted_controls():
+    """Planted controls: a group with one member's scales swapped, and one with
+    one member's suh swapped, must change that member's bytes."""
+    K, M = 5120, 7
+    x = G.dev_bf16(G.xbits("control", M, K))
+    a = G.layer("control", "a", K, 1024, 4)
+    b = G.layer("control", "b", K, 1024, 4)
+    wa, wb = G.upload(a), G.upload(b)
+    ya, yb = [G.host_u16(t) for t in G.run_group([wa, wb], x, tag="control")]
+    swapped = ex().Weight(wa.words, wb.scales, wa.suh, wa.svh, K, 1024, 4)
+    assert not np.array_equal(G.host_u16(G.run_group([swapped, wb], x, tag="scales swapped")[0]), ya)
+    swapped_suh = ex().Weight(wa.words, wa.scales, wb.suh, wa.svh, K, 1024, 4)
+    assert not np.array_equal(G.host_u16(G.run_group([swapped_suh, wb], x, tag="suh swapped")[0]), ya)
+
+
+def test_another_k_split_changes_bits():
+    """Planted control 'another K split': forcing S away from the plan must
+    change some bytes (so the bitwise tests can see a reduction-order change),
+    while staying within the oracle tolerance."""
+    K, N, M = 5120, 1024, 16
+    L = G.layer("split", "k", K, N, 4)
+    w = G.upload(L)
+    x = G.xbits("split", M, K)
+    xd = G.dev_bf16(x)
+    base = G.host_u16(G.run(w, xd, tag="plan"))
+    S = ex().exl3_plan(K, N, 4).splits
+    other = 8 if S != 8 else 16
+    ex().exl3_test_force(-1, -1, other)
+    y = G.host_u16(G.run(w, xd, tag=f"forced S={other}"))
+    ex().exl3_test_force(-1, -1, 0)
+    assert not np.array_equal(y, base)
+    G.assert_close(y, O.linear_packed(L.words, K, N, 4, L.scales, L.suh, L.svh, x), what="forced split")
+
+
+def test_views_equal_full_head_columns():
+    """PR #1507: span views of >= 64 blocks plan as the whole head, so their
+    output is the head's output byte for byte; a 3-block view plans otherwise
+    and is the control that goes red. Full 6-bit head 5120 -> 248,320, M = 16."""
+    K, N, M = 5120, synth.VOCAB, 16
+    L = G.layer("views", "head", K, N, 6)
+    w = G.upload(L)
+    xd = G.dev_bf16(G.xbits("views", M, K))
+    full = G.host_u16(G.run(w, xd, tag="full head"))
+    a = G.host_u16(G.run(w.columns(0, 98304), xd, tag="span A"))
+    b = G.host_u16(G.run(w.columns(240128, 8192), xd, tag="span B"))
+    assert np.array_equal(a, full[:, :98304])
+    assert np.array_equal(b, full[:, 240128:])
+    kept = b[:, 248032 - 240128:]
+    assert kept.shape[1] == 288 and np.array_equal(kept, full[:, 248032:])
+    tail3 = G.host_u16(G.run(w.columns(248320 - 384, 384), xd, tag="3-block tail"))
+    assert ex().exl3_plan(K, 384, 6).splits != ex().exl3_plan(K, N, 6).splits
+    assert not np.array_equal(tail3, full[:, -384:])
+
+
+def test_counters_zero_at_rest_and_repeats_identical():
+    """Counters are reset by each block's last arriver: zero after every call
+    without any memset between calls; 200 repeats give identical bytes."""
+    torch = G.torch_mod()
+    K, N = 5120, 1024
+    L = G.layer("repeat", "k", K, N, 4)
+    w = G.upload(L)
+    xd = G.dev_bf16(G.xbits("repeat", 16, K))
+    ws = ex().Workspace().reserve([w], 128)
+    first = None
+    for it in range(200):
+        y = G.empty_y(16, N)
+        if it % 50 == 0:
+            G.say(f"repeat {it}")
+        ex().exl3_linear(w, xd, y, ws)
+        if first is None:
+            first = G.host_u16(y)
+        elif it % 20 == 0 or it == 199:
+            assert np.array_equal(G.host_u16(y), first), it
+    torch.cuda.synchronize()
+    assert int(ws.counters().abs().sum()) == 0
+    # other row counts through the same workspace: still zero at rest
+    for M in (1, 17, 64, 128):
+        y = G.empty_y(M, N)
+        ex().exl3_linear(w, G.dev_bf16(G.xbits("repeat", M, K)), y, ws)
+        torch.cuda.synchronize()
+        assert int(ws.counters().abs().sum()) == 0, M
+
+
+def test_two_streams_equal_solo():
+    """Concurrent == solo: two streams with their own workspaces."""
+    torch = G.torch_mod()
+    K = 5120
+    La, Lb = G.layer("streams", "a", K, 1024, 4), G.layer("streams", "b", K, 6144, 4)
+    wa, wb = G.upload(La), G.upload(Lb)
+    xd = G.dev_bf16(G.xbits("streams", 16, K))
+    solo_a = G.host_u16(G.run(wa, xd, tag="solo a"))
+    solo_b = G.host_u16(G.run(wb, xd, tag="solo b"))
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    ws1 = ex().Workspace().reserve([wa], 16, stream=s1)
+    ws2 = ex().Workspace().reserve([wb], 16, stream=s2)
+    torch.cuda.synchronize()
+    ya, yb = G.empty_y(16, 1024), G.empty_y(16, 6144)
+    G.say("two streams x 50")
+    for _ in range(50):
+        ex().exl3_linear(wa, xd, ya, ws1, stream=s1)
+        ex().exl3_linear(wb, xd, yb, ws2, stream=s2)
+    torch.cuda.synchronize()
+    assert np.array_equal(G.host_u16(ya), solo_a) and np.array_equal(G.host_u16(yb), solo_b)
+
+
+def test_split_exchange_stress():
+    """Race check of the counter protocol: 2000 back-to-back calls of a narrow
+    weight (32 splits per block, exchange through partials) on one stream,
+    bytes compared every 100 calls and counters zero at the end."""
+    torch = G.torch_mod()
+    K, N = 5120, 1024
+    L = G.layer("stress", "k", K, N, 4)
+    w = G.upload(L)
+    xd = G.dev_bf16(G.xbits("stress", 16, K))
+    ex().exl3_test_force(-1, 0, 0)
+    ws = ex().Workspace().reserve([w], 16)
+    ref = G.host_u16(G.run(w, xd, ws=ws, tag="stress ref"))
+    ys = [G.empty_y(16, N) for _ in range(100)]
+    for rep in range(20):
+        G.say(f"stress batch {rep}")
+        for y in ys:
+            ex().exl3_linear(w, xd, y, ws)
+        torch.cuda.synchronize()
+        for y in ys:
+            assert np.array_equal(G.host_u16(y), ref), rep
+    ex().exl3_test_force(-1, -1, 0)
+    assert int(ws.counters().abs().sum()) == 0

@@ -1,0 +1,283 @@
+"""Host logic of libexl3.so, on the CPU (no kernel runs here).
+
+The library loads without a GPU; plan, views, workspace sizing and every
+argument check are host code. With the mock driver on, launches and counter
+fills are recorded instead of issued, so the launch/fill accounting of the
+pages' host tests can be checked here (TensorFold PR #1475: counters zeroed
+on the call's stream only when they grow; PR #1467: after reserve a call
+allocates nothing and zeroes nothing).
+"""
+
+import ctypes
+import re
+
+import pytest
+
+import trellis_quantized_linear_amd.exl3 as ex
+from trellis_quantized_linear_amd import synth
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return ex.lib()
+
+
+@pytest.fixture(autouse=True)
+def _reset_hooks(lib):
+    ex.exl3_test_force(-1, -1, 0)
+    ex.exl3_test_mock(False)
+    ex.exl3_test_mock_counts()
+    yield
+    ex.exl3_test_force(-1, -1, 0)
+    ex.exl3_test_mock(False)
+    ex.exl3_test_mock_counts()
+
+
+def fake_weight(K, N, bits, base=0x10000000, block_stride=None):
+    """A descriptor with plausible (never dereferenced) device addresses."""
+    bs = block_stride if block_stride is not None else 16 * K * bits
+    d = ex.exl3_weight_t(base, base + 0x4000000, base + 0x8000000, base + 0xC000000, K, N, bs, bits, 0)
+    return ex.Weight(None, None, None, None, K, N, bits, _desc=d)
+
+
+def test_exports_every_declared_symbol(lib):
+    text = open(ex.HEADER).read()
+    names = sorted(set(re.findall(r"^\s*(?:int|const char \*)\s*(exl3_\w+)\s*\(", text, re.M)))
+    assert len(names) == 15
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(ex._SIGNATURES), set(names) ^ set(ex._SIGNATURES)
+
+
+def test_plan_basic_and_m_independent(lib):
+    p = ex.exl3_plan(5120, 6144, 4)
+    assert p.waves == 4 and p.chunks == 160 and p.n_blocks == 48
+    # the plan takes no row count: the same for every caller at any M
+    assert ex.exl3_plan(5120, 6144, 4).splits == p.splits
+
+
+def test_plan_wide_threshold_head_views(lib):
+    """PR #1507: the 98,304-column span and the 64-block tail plan as the whole
+    248,320-column head; a 3-block (384-column) tail does not ('expected 1,
+    found 8' on the pages)."""
+    head = ex.exl3_plan(5120, 248320, 6).splits
+    assert ex.exl3_plan(5120, 98304, 6).splits == head
+    assert ex.exl3_plan(5120, 8192, 6).splits == head
+    assert ex.exl3_plan(5120, 64 * 128, 6).splits == head
+    assert ex.exl3_plan(5120, 384, 6).splits != head
+    assert ex.exl3_plan(5120, 63 * 128, 6).splits != head or head == 1
+
+
+def test_plan_every_wide_n_equal(lib):
+    for K in (256, 1024, 5120, 17408):
+        s = {ex.exl3_plan(K, nb * 128, 4).splits for nb in (64, 65, 100, 136, 768, 1940, 4096)}
+        assert len(s) == 1, (K, s)
+
+
+def test_plan_table_fills_the_gpu(lib):
+    # narrow weights split until 256 workgroups or 4 chunks per split
+    for K, N in ((5120, 1024), (5120, 6144), (17408, 5120), (256, 256)):
+        p = ex.exl3_plan(K, N, 4)
+        assert p.n_blocks * p.splits >= 256 or p.chunks // p.splits < 8 or p.splits == 32
+        assert p.chunks // p.splits >= 4
+
+
+def test_plan_errors(lib):
+    out = ex.exl3_plan_t()
+    assert lib.exl3_plan(5120, 6144, 1, ctypes.byref(out)) == ex.EXL3_EBITS
+    assert lib.exl3_plan(5120, 6144, 9, ctypes.byref(out)) == ex.EXL3_EBITS
+    assert lib.exl3_plan(5000, 6144, 4, ctypes.byref(out)) == ex.EXL3_EALIGN
+    assert lib.exl3_plan(5120, 6100, 4, ctypes.byref(out)) == ex.EXL3_EALIGN
+    assert lib.exl3_plan(0, 128, 4, ctypes.byref(out)) == ex.EXL3_EALIGN
+    assert lib.exl3_plan(5120, 6144, 4, None) == ex.EXL3_EINVAL
+
+
+def test_view_keeps_parent_strides_and_moves_to_first_block(lib):
+    """PR #1507 host test: a column view keeps the parent's strides and moves
+    to its first 128-column block."""
+    w = fake_weight(5120, 248320, 6)
+    v = w.columns(240128, 8192)
+    bs = 16 * 5120 * 6
+    assert v.desc.block_stride == w.desc.block_stride == bs
+    assert v.desc.words == w.desc.words + (240128 // 128) * bs
+    assert v.desc.scales == w.desc.scales + 2 * 240128
+    assert v.desc.svh == w.desc.svh + 2 * 240128
+    assert v.desc.suh == w.desc.suh
+    assert v.desc.K == 5120 and v.desc.N == 8192 and v.desc.bits == 6
+    # a view of a view composes
+    vv = v.columns(128, 256)
+    assert vv.desc.words == w.desc.words + (240128 // 128 + 1) * bs and vv.desc.N == 256
+
+
+def test_view_errors(lib):
+    w = fake_weight(512, 1024, 4)
+    out = ex.exl3_weight_t()
+    f = lib.exl3_weight_columns
+    assert f(ctypes.byref(w.desc), 64, 128, ctypes.byref(out)) == ex.EXL3_EALIGN
+    assert f(ctypes.byref(w.desc), 0, 100, ctypes.byref(out)) == ex.EXL3_EALIGN
+    assert f(ctypes.byref(w.desc), 896, 256, ctypes.byref(out)) == ex.EXL3_ERANGE
+    assert f(ctypes.byref(w.desc), 0, 0, ctypes.byref(out)) == ex.EXL3_EINVAL
+    assert f(ctypes.byref(w.desc), -128, 128, ctypes.byref(out)) == ex.EXL3_EINVAL
+    assert f(None, 0, 128, ctypes.byref(out)) == ex.EXL3_EINVAL
+    assert f(ctypes.byref(w.desc), 0, 1024, ctypes.byref(out)) == ex.EXL3_OK
+
+
+def test_descriptor_errors(lib):
+    ws = ex.exl3_workspace_t(0x20000000, 1 << 30, 1 << 20)
+    x, y = 0x30000000, 0x40000000
+
+    def call(d, M=4, ldx=None, ldy=None):
+        return lib.exl3_linear(ctypes.byref(d), x, ldx or d.K, M, y, ldy or d.N, ctypes.byref(ws), None)
+
+    ex.exl3_test_mock(True)
+    good = fake_weight(512, 256, 4).desc
+    assert call(good) == ex.EXL3_OK
+    for field, val, code in (("bits", 1, ex.EXL3_EBITS), ("bits", 9, ex.EXL3_EBITS), ("K", 500, ex.EXL3_EALIGN),
+                             ("N", 200, ex.EXL3_EALIGN), ("block_stride", 100, ex.EXL3_EALIGN),
+                             ("words", 0x10000002, ex.EXL3_EALIGN), ("scales", 0x10000001, ex.EXL3_EALIGN),
+                             ("words", 0, ex.EXL3_EINVAL), ("flags", 1, ex.EXL3_EINVAL)):
+        d = fake_weight(512, 256, 4).desc
+        setattr(d, field, val)
+        assert call(d) == code, (field, val)
+    assert call(good, M=-1) == ex.EXL3_EINVAL
+    assert call(good, ldx=256) == ex.EXL3_EINVAL
+    assert call(good, ldy=128) == ex.EXL3_EINVAL
+    assert lib.exl3_linear(ctypes.byref(good), x + 1, 512, 4, y, 256, ctypes.byref(ws), None) == ex.EXL3_EALIGN
+    assert lib.exl3_linear(ctypes.byref(good), None, 512, 4, y, 256, ctypes.byref(ws), None) == ex.EXL3_EINVAL
+    assert lib.exl3_linear(ctypes.byref(good), x, 512, 4, None, 256, ctypes.byref(ws), None) == ex.EXL3_EINVAL
+    assert lib.exl3_linear(ctypes.byref(good), x, 512, 4, y, 256, None, None) == ex.EXL3_EWORKSPACE
+    launches, fills, _, _ = ex.exl3_test_mock_counts()
+    assert launches == 2 and fills == 0      # only the one good call launched (rotation + linear)
+
+
+def test_m_zero_launches_nothing(lib):
+    ex.exl3_test_mock(True)
+    d = fake_weight(512, 256, 4).desc
+    ws = ex.exl3_workspace_t(0, 0, 0)        # not even a workspace is needed
+    assert lib.exl3_linear(ctypes.byref(d), 0x30000000, 512, 0, 0x40000000, 256, ctypes.byref(ws), None) == 0
+    assert ex.exl3_test_mock_counts()[:2] == (0, 0)
+
+
+def test_group_errors(lib):
+    ex.exl3_test_mock(True)
+    a = fake_weight(5120, 6144, 4)
+    b = fake_weight(5120, 1024, 4, base=0x50000000)
+    c = fake_weight(5120, 1024, 3, base=0x60000000)
+    d = fake_weight(4096, 1024, 4, base=0x70000000)
+    need, _ = ex.exl3_workspace_need([a, b, b], 16)
+    ws = ex.exl3_workspace_t(0x20000000, need + (1 << 20), 1 << 20)
+
+    def group(members, M=16):
+        arr = ex._wlist(members)
+        ys = (ctypes.c_void_p * len(members))(*[0x80000000] * len(members))
+        ld = (ctypes.c_int64 * len(members))(*[m.N for m in members])
+        return lib.exl3_linear_group(len(members), arr, 0x30000000, 5120, M, ys, ld, ctypes.byref(ws), None)
+
+    assert group([a, b, b]) == ex.EXL3_OK
+    assert group([a, c]) == ex.EXL3_EGROUP          # different bits
+    assert group([a, d]) == ex.EXL3_EGROUP          # different K
+    assert group([a, b, b, b]) == ex.EXL3_EGROUP    # more than three
+    assert lib.exl3_linear_group(0, None, 0x30000000, 5120, 16, None, None, ctypes.byref(ws), None) == ex.EXL3_EGROUP
+    launches, fills, _, _ = ex.exl3_test_mock_counts()
+    assert launches == 2 and fills == 0             # one rotation + one linear for the whole group
+
+
+def test_workspace_zeroed_once_per_growth_on_the_given_stream(lib):
+    """PR #1475 host test: one fill per growth, on the named stream, and none
+    while the buffer is big enough; linear calls never fill."""
+    ex.exl3_test_mock(True)
+    w = fake_weight(5120, 1024, 4)
+    need, cb = ex.exl3_workspace_need([w], 16)
+    assert cb > 0 and need > cb
+    ws = ex.exl3_workspace_t(0, 0, 0)
+    stream = 0xABC000
+    assert lib.exl3_workspace_grow(ctypes.byref(ws), 0x20000000, need, cb, stream) == ex.EXL3_OK
+    launches, fills, fbytes, s = ex.exl3_test_mock_counts()
+    assert (launches, fills, fbytes, s) == (0, 1, cb, stream)
+    # the same size again is not a growth: refused, nothing issued
+    assert lib.exl3_workspace_grow(ctypes.byref(ws), 0x21000000, need, cb, stream) == ex.EXL3_EWORKSPACE
+    assert ex.exl3_test_mock_counts()[:2] == (0, 0)
+    # steady state: every call at 1..16 rows launches two kernels, fills nothing
+    for M in range(1, 17):
+        assert lib.exl3_linear(ctypes.byref(w.desc), 0x30000000, 5120, M, 0x40000000, 1024, ctypes.byref(ws),
+                               0x123000) == 0
+    launches, fills, _, s = ex.exl3_test_mock_counts()
+    assert launches == 32 and fills == 0 and s == 0x123000
+    # a larger buffer grows once more, again on the named stream
+    assert lib.exl3_workspace_grow(ctypes.byref(ws), 0x22000000, 2 * need, 2 * cb, 0xDEF000) == ex.EXL3_OK
+    assert ex.exl3_test_mock_counts()[1:] == (1, 2 * cb, 0xDEF000)
+
+
+def test_workspace_too_small_is_refused(lib):
+    ex.exl3_test_mock(True)
+    w = fake_weight(5120, 1024, 4)
+    need, cb = ex.exl3_workspace_need([w], 16)
+    ws = ex.exl3_workspace_t(0x20000000, need - 256, cb)
+    assert lib.exl3_linear(ctypes.byref(w.desc), 0x30000000, 5120, 16, 0x40000000, 1024, ctypes.byref(ws),
+                           None) == ex.EXL3_EWORKSPACE
+    ws = ex.exl3_workspace_t(0x20000000, need, 0)
+    assert lib.exl3_linear(ctypes.byref(w.desc), 0x30000000, 5120, 16, 0x40000000, 1024, ctypes.byref(ws),
+                           None) == ex.EXL3_EWORKSPACE
+    assert ex.exl3_test_mock_counts()[0] == 0
+
+
+def test_workspace_for_max_rows_covers_smaller_calls(lib):
+    ex.exl3_test_mock(True)
+    shapes = [(5120, 1024), (5120, 6144), (5120, 17408), (17408, 5120), (5120, 248320)]
+    for K, N in shapes:
+        w = fake_weight(K, N, 4)
+        for max_rows in (16, 100, 128, 300, 8192):
+            need, cb = ex.exl3_workspace_need([w], max_rows)
+            for M in sorted({1, 7, 16, 17, 33, 64, 100, 128, 129, 256, max_rows}):
+                if M > max_rows:
+                    continue
+                n2, c2 = ex.exl3_workspace_need([w], M)
+                assert n2 <= need and c2 <= cb, (K, N, max_rows, M)
+
+
+def test_workspace_grow_errors(lib):
+    ws = ex.exl3_workspace_t(0, 0, 0)
+    assert lib.exl3_workspace_grow(ctypes.byref(ws), 0x20000001, 1024, 256, None) == ex.EXL3_EALIGN
+    assert lib.exl3_workspace_grow(ctypes.byref(ws), 0x20000000, 1024, 100, None) == ex.EXL3_EALIGN
+    assert lib.exl3_workspace_grow(ctypes.byref(ws), 0x20000000, 256, 512, None) == ex.EXL3_EWORKSPACE
+    assert lib.exl3_workspace_grow(None, 0x20000000, 1024, 256, None) == ex.EXL3_EINVAL
+    assert lib.exl3_workspace_grow(ctypes.byref(ws), None, 1024, 256, None) == ex.EXL3_EINVAL
+
+
+def test_strerror_covers_every_code(lib):
+    for code in range(0, -8, -1):
+        assert lib.exl3_strerror(code) != b"unknown error"
+    assert lib.exl3_strerror(-99) == b"unknown error"
+
+
+def test_test_force_validation(lib):
+    assert lib.exl3_test_force(3, -1, 0) == ex.EXL3_EINVAL
+    assert lib.exl3_test_force(-1, 2, 0) == ex.EXL3_EINVAL
+    assert lib.exl3_test_force(-1, -1, -1) == ex.EXL3_EINVAL
+    assert lib.exl3_test_force(8, 1, 4) == ex.EXL3_OK
+
+
+def test_dispatch_sweep_reaches_only_built_forms(lib):
+    """The pages' dispatch sweep (PR #1467 follow-up): K and N from 128 to
+    16384 at 1..128 rows through the host dispatch; every call must be
+    accepted (the kernel table covers every width x row tiling x launch
+    shape), with a workspace sized by exl3_workspace_need."""
+    ex.exl3_test_mock(True)
+    for bits in (2, 3, 4, 5, 6, 7, 8):
+        for K in (128, 512, 1408, 5120, 16384):
+            for N in (128, 1024, 8192, 16384):
+                w = fake_weight(K, N, bits)
+                need, cb = ex.exl3_workspace_need([w], 128)
+                ws = ex.exl3_workspace_t(0x20000000, need, cb)
+                for M in (1, 16, 17, 48, 49, 128):
+                    rc = lib.exl3_linear(ctypes.byref(w.desc), 0x30000000, K, M, 0x40000000, N, ctypes.byref(ws), None)
+                    assert rc == 0, (bits, K, N, M, rc)
+    ex.exl3_test_mock_counts()
+
+
+def test_synth_is_seeded_and_shaped():
+    a = synth.gen_layer("cfg", "q", 256, 384, 3)
+    b = synth.gen_layer("cfg", "q", 256, 384, 3)
+    assert (a.words == b.words).all() and (a.scales == b.scales).all()
+    assert a.words.size == 256 * 384 * 3 // 8 and a.scales.size == 384 and a.suh.size == 256
+    assert set(a.suh.tolist()) <= {0x3C00, 0xBC00}

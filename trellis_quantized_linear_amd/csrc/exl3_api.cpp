@@ -1,0 +1,402 @@
+// Host side of the EXL3 linear: argument checks, the K-split plan, column
+// views, workspace layout and growth, regime choice and launches. The C ABI
+// is declared in include/exl3.h.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cstring>
+
+#include "exl3.h"
+#include "exl3_internal.h"
+
+namespace {
+
+using exl3::kBlockCols;
+using exl3::kChunk;
+using exl3::kMaxMembers;
+
+thread_local int g_last_hip = 0;
+
+// Test hooks (process-global; documented as not thread-safe).
+struct TestHooks {
+  int m_tiles = -1;
+  int chained = -1;
+  int splits = 0;
+  bool mock = false;
+  int64_t launches = 0;
+  int64_t fills = 0;
+  int64_t fill_bytes = 0;
+  void *last_stream = nullptr;
+};
+TestHooks g_hooks;
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+int hip_fail(int err) {
+  g_last_hip = err;
+  return EXL3_EHIP;
+}
+
+int check_weight(const exl3_weight_t *w) {
+  if (!w || !w->words || !w->scales || !w->suh || !w->svh) return EXL3_EINVAL;
+  if (w->flags != 0) return EXL3_EINVAL;
+  if (w->bits < 2 || w->bits > 8) return EXL3_EBITS;
+  if (w->K <= 0 || w->N <= 0 || w->K % 128 != 0 || w->N % 128 != 0) return EXL3_EALIGN;
+  // keep every in-kernel byte offset of a block inside 32 bits
+  if (w->K > (int64_t(1) << 24) || w->N / kBlockCols > (int64_t(1) << 30)) return EXL3_EINVAL;
+  if (w->block_stride < 16 * w->K * w->bits || w->block_stride % 4 != 0) return EXL3_EALIGN;
+  if ((uintptr_t)w->words % 4 != 0) return EXL3_EALIGN;
+  if ((uintptr_t)w->scales % 2 != 0 || (uintptr_t)w->suh % 2 != 0 || (uintptr_t)w->svh % 2 != 0)
+    return EXL3_EALIGN;
+  return EXL3_OK;
+}
+
+// The plan table. S depends on (K, N, bits) only. Targets for 256 CUs:
+//  * a weight of at least EXL3_WIDE_BLOCKS blocks takes S_wide(K), so every
+//    such view plans alike; S_wide(K) = 4 once K has 32 chunks per split
+//    (K >= 4096), giving a 64-block view 256 workgroups;
+//  * a narrower weight takes the smallest power of two with n_blocks*S >= 256,
+//    at most 32 and keeping at least 4 chunks (128 K) per split.
+int32_t splits_for(int64_t K, int64_t N, int32_t bits) {
+  (void)bits;
+  const int64_t chunks = K / kChunk;
+  const int64_t nb = N / kBlockCols;
+  int32_t s = 1;
+  if (nb >= EXL3_WIDE_BLOCKS) {
+    while (s < 4 && chunks / (2 * s) >= 32) s *= 2;
+    return s;
+  }
+  while (nb * s < 256 && s < 32 && chunks / (2 * s) >= 4) s *= 2;
+  return s;
+}
+
+struct MemberPlan {
+  const exl3_weight_t *w;
+  int32_t splits;
+  int32_t n_blocks;
+};
+
+struct Launch {
+  int m_tiles;
+  bool chained;
+  int64_t row_blocks;
+};
+
+Launch choose_launch(const MemberPlan *mp, int n, int64_t M) {
+  Launch L;
+  int mt = g_hooks.m_tiles;
+  if (mt != 1 && mt != 2 && mt != 4 && mt != 8) mt = M <= 16 ? 1 : M <= 32 ? 2 : M <= 64 ? 4 : 8;
+  L.m_tiles = mt;
+  L.row_blocks = (M + 16 * mt - 1) / (16 * mt);
+  bool all_single = true;
+  int64_t blocks = 0;
+  for (int j = 0; j < n; ++j) {
+    all_single = all_single && mp[j].splits == 1;
+    blocks += mp[j].n_blocks;
+  }
+  if (g_hooks.chained == 0 || g_hooks.chained == 1) {
+    L.chained = g_hooks.chained == 1;
+  } else {
+    // partials and counters only when the grid would otherwise be too small
+    // to stream HBM: prompt row blocks and wide weights give enough
+    // workgroups by themselves.
+    L.chained = all_single || M > 128 || L.row_blocks * blocks >= 512;
+  }
+  return L;
+}
+
+struct Layout {
+  size_t counters;          // uint32 counters used
+  size_t xr_bytes[kMaxMembers];
+  size_t part_bytes[kMaxMembers];
+  size_t rest;              // bytes after the counter region
+};
+
+Layout layout_for(const MemberPlan *mp, int n, int64_t M, int64_t K, const Launch &L) {
+  Layout lay{};
+  for (int j = 0; j < n; ++j) {
+    lay.xr_bytes[j] = align_up((size_t)M * K * 2);
+    if (!L.chained) {
+      lay.part_bytes[j] = align_up((size_t)mp[j].splits * M * mp[j].w->N * 4);
+      lay.counters += (size_t)L.row_blocks * mp[j].n_blocks;
+    }
+    lay.rest += lay.xr_bytes[j] + lay.part_bytes[j];
+  }
+  return lay;
+}
+
+int check_group(int32_t n, const exl3_weight_t *const *w, int64_t M, MemberPlan *mp) {
+  if (n < 1 || n > kMaxMembers || !w) return EXL3_EGROUP;
+  if (M < 0) return EXL3_EINVAL;
+  for (int j = 0; j < n; ++j) {
+    const int e = check_weight(w[j]);
+    if (e != EXL3_OK) return e;
+    if (j > 0 && (w[j]->K != w[0]->K || w[j]->bits != w[0]->bits)) return EXL3_EGROUP;
+    mp[j].w = w[j];
+    mp[j].splits = g_hooks.splits > 0 ? g_hooks.splits : splits_for(w[j]->K, w[j]->N, w[j]->bits);
+    mp[j].n_blocks = (int32_t)(w[j]->N / kBlockCols);
+    if (mp[j].splits > w[j]->K / kChunk) return EXL3_EINVAL;
+  }
+  // rotated input offsets of one member stay inside a 32-bit buffer range
+  if (M > 0 && (uint64_t)M * w[0]->K * 2 >= (uint64_t(1) << 31)) return EXL3_EINVAL;
+  return EXL3_OK;
+}
+
+void fill_need(const MemberPlan *mp, int n, int64_t M, size_t *bytes, size_t *counter_bytes) {
+  const Launch L = choose_launch(mp, n, M);
+  const Layout lay = layout_for(mp, n, M, mp[0].w->K, L);
+  const size_t cb = align_up(lay.counters * 4);
+  if (counter_bytes) *counter_bytes = std::max(*counter_bytes, cb);
+  if (bytes) *bytes = std::max(*bytes, cb + lay.rest);
+}
+
+int issue_fill(void *ptr, size_t bytes, void *stream) {
+  if (g_hooks.mock) {
+    g_hooks.fills += 1;
+    g_hooks.fill_bytes += (int64_t)bytes;
+    g_hooks.last_stream = stream;
+    return EXL3_OK;
+  }
+  const int e = exl3::launch_fill_zero(ptr, bytes, stream);
+  return e ? hip_fail(e) : EXL3_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int exl3_plan(int64_t K, int64_t N, int32_t bits, exl3_plan_t *out) {
+  if (!out) return EXL3_EINVAL;
+  if (bits < 2 || bits > 8) return EXL3_EBITS;
+  if (K <= 0 || N <= 0 || K % 128 != 0 || N % 128 != 0) return EXL3_EALIGN;
+  out->splits = splits_for(K, N, bits);
+  out->waves = exl3::kWaves;
+  out->chunks = K / kChunk;
+  out->n_blocks = N / kBlockCols;
+  return EXL3_OK;
+}
+
+int exl3_weight_columns(const exl3_weight_t *parent, int64_t col_from, int64_t n_cols, exl3_weight_t *view) {
+  if (!parent || !view) return EXL3_EINVAL;
+  const int e = check_weight(parent);
+  if (e != EXL3_OK) return e;
+  if (n_cols <= 0 || col_from < 0) return EXL3_EINVAL;
+  if (col_from % kBlockCols != 0 || n_cols % kBlockCols != 0) return EXL3_EALIGN;
+  if (col_from + n_cols > parent->N) return EXL3_ERANGE;
+  exl3_weight_t v = *parent;
+  v.words = (const uint8_t *)parent->words + (col_from / kBlockCols) * parent->block_stride;
+  v.scales = (const uint16_t *)parent->scales + col_from;
+  v.svh = (const uint16_t *)parent->svh + col_from;
+  v.N = n_cols;
+  *view = v;
+  return EXL3_OK;
+}
+
+int exl3_workspace_need(int32_t n_members, const exl3_weight_t *const *w, int64_t M, size_t *bytes,
+                        size_t *counter_bytes) {
+  if (!bytes || !counter_bytes) return EXL3_EINVAL;
+  MemberPlan mp[kMaxMembers];
+  const int e = check_group(n_members, w, M, mp);
+  if (e != EXL3_OK) return e;
+  *bytes = 0;
+  *counter_bytes = 0;
+  // sizes grow with M inside each regime; the regime boundaries and M itself
+  // bound every smaller call
+  const int64_t probes[3] = {std::min<int64_t>(M, 16), std::min<int64_t>(M, 128), M};
+  for (int64_t p : probes)
+    if (p > 0) fill_need(mp, n_members, p, bytes, counter_bytes);
+  if (*bytes < *counter_bytes) *bytes = *counter_bytes;
+  return EXL3_OK;
+}
+
+int exl3_workspace_grow(exl3_workspace_t *ws, void *ptr, size_t bytes, size_t counter_bytes, void *stream) {
+  if (!ws || !ptr) return EXL3_EINVAL;
+  if ((uintptr_t)ptr % kAlign != 0 || counter_bytes % kAlign != 0) return EXL3_EALIGN;
+  if (counter_bytes > bytes) return EXL3_EWORKSPACE;
+  if (bytes <= ws->bytes && counter_bytes <= ws->counter_bytes) return EXL3_EWORKSPACE;
+  const int e = issue_fill(ptr, counter_bytes, stream);
+  if (e != EXL3_OK) return e;
+  ws->ptr = ptr;
+  ws->bytes = bytes;
+  ws->counter_bytes = counter_bytes;
+  return EXL3_OK;
+}
+
+int exl3_workspace_reset(const exl3_workspace_t *ws, void *stream) {
+  if (!ws || !ws->ptr) return EXL3_EINVAL;
+  return issue_fill(ws->ptr, ws->counter_bytes, stream);
+}
+
+int exl3_linear_group(int32_t n_members, const exl3_weight_t *const *w, const void *x, int64_t ldx, int64_t M,
+                      void *const *y, const int64_t *ldy, const exl3_workspace_t *ws, void *stream) {
+  MemberPlan mp[kMaxMembers];
+  int e = check_group(n_members, w, M, mp);
+  if (e != EXL3_OK) return e;
+  if (!y || !ldy) return EXL3_EINVAL;
+  if (M == 0) return EXL3_OK;
+  const int64_t K = w[0]->K;
+  if (!x || ldx < K || (uintptr_t)x % 2 != 0) return x && ldx >= K ? EXL3_EALIGN : EXL3_EINVAL;
+  for (int j = 0; j < n_members; ++j) {
+    if (!y[j] || ldy[j] < w[j]->N) return EXL3_EINVAL;
+    if ((uintptr_t)y[j] % 2 != 0) return EXL3_EALIGN;
+  }
+  if (!ws || !ws->ptr) return EXL3_EWORKSPACE;
+
+  const Launch L = choose_launch(mp, n_members, M);
+  const Layout lay = layout_for(mp, n_members, M, K, L);
+  if (lay.counters * 4 > ws->counter_bytes || ws->counter_bytes + lay.rest > ws->bytes) return EXL3_EWORKSPACE;
+
+  exl3::RotArgs ra{};
+  exl3::LinearArgs la{};
+  uint8_t *base = (uint8_t *)ws->ptr;
+  size_t off = ws->counter_bytes;
+  size_t counter_off = 0;
+  int64_t wg = 0;
+  for (int j = 0; j < n_members; ++j) {
+    const exl3_weight_t *wj = w[j];
+    uint16_t *xr = (uint16_t *)(base + off);
+    off += lay.xr_bytes[j];
+    ra.suh[j] = (const uint16_t *)wj->suh;
+    ra.xr[j] = xr;
+    exl3::MemberArgs &m = la.m[j];
+    m.words = (const uint8_t *)wj->words;
+    m.scales = (const uint16_t *)wj->scales;
+    m.svh = (const uint16_t *)wj->svh;
+    m.xr = xr;
+    m.y = (uint16_t *)y[j];
+    m.ldy = ldy[j];
+    m.block_stride = wj->block_stride;
+    m.N = (int32_t)wj->N;
+    m.n_blocks = mp[j].n_blocks;
+    m.splits = mp[j].splits;
+    m.wg_begin = (int32_t)wg;
+    if (!L.chained) {
+      m.partials = (float *)(base + off);
+      off += lay.part_bytes[j];
+      m.counters = (uint32_t *)base + counter_off;
+      counter_off += (size_t)L.row_blocks * mp[j].n_blocks;
+      wg += L.row_blocks * mp[j].n_blocks * mp[j].splits;
+    } else {
+      wg += L.row_blocks * mp[j].n_blocks;
+    }
+  }
+  if (wg >= (int64_t(1) << 31)) return EXL3_EINVAL;
+  ra.x = (const uint16_t *)x;
+  ra.ldx = ldx;
+  ra.M = (int32_t)M;
+  ra.K = (int32_t)K;
+  ra.n_members = n_members;
+  ra.natural_order = 0;
+  la.n_members = n_members;
+  la.M = (int32_t)M;
+  la.K = (int32_t)K;
+  la.chunks = (int32_t)(K / kChunk);
+  la.row_blocks = (int32_t)L.row_blocks;
+  la.total_wgs = (int32_t)wg;
+
+  if (g_hooks.mock) {
+    g_hooks.launches += 2;
+    g_hooks.last_stream = stream;
+    return EXL3_OK;
+  }
+  e = exl3::launch_rot(ra, stream);
+  if (e) return hip_fail(e);
+  e = exl3::launch_linear(la, w[0]->bits, L.m_tiles, L.chained, stream);
+  if (e) return hip_fail(e);
+  return EXL3_OK;
+}
+
+int exl3_linear(const exl3_weight_t *w, const void *x, int64_t ldx, int64_t M, void *y, int64_t ldy,
+                const exl3_workspace_t *ws, void *stream) {
+  const exl3_weight_t *ws_[1] = {w};
+  void *ys[1] = {y};
+  const int64_t ldys[1] = {ldy};
+  return exl3_linear_group(1, ws_, x, ldx, M, ys, ldys, ws, stream);
+}
+
+const char *exl3_strerror(int code) {
+  switch (code) {
+    case EXL3_OK: return "ok";
+    case EXL3_EINVAL: return "invalid argument (null pointer, negative size or leading dimension too small)";
+    case EXL3_EALIGN: return "alignment: K and N must be multiples of 128, views whole 128-column blocks, pointers aligned";
+    case EXL3_ERANGE: return "column view outside its parent";
+    case EXL3_EBITS: return "bits per weight outside 2..8";
+    case EXL3_EWORKSPACE: return "workspace missing or too small for this call";
+    case EXL3_EGROUP: return "group must have 1..3 members of one K and one bit width";
+    case EXL3_EHIP: return "a HIP launch failed (see exl3_last_hip_error)";
+    default: return "unknown error";
+  }
+}
+
+int exl3_last_hip_error(void) { return g_last_hip; }
+
+int exl3_test_dequant(const exl3_weight_t *w, void *out_fp16, void *stream) {
+  const int e = check_weight(w);
+  if (e != EXL3_OK) return e;
+  if (!out_fp16) return EXL3_EINVAL;
+  exl3::DequantArgs a{};
+  a.words = (const uint8_t *)w->words;
+  a.out = (uint16_t *)out_fp16;
+  a.block_stride = w->block_stride;
+  a.K = (int32_t)w->K;
+  a.N = (int32_t)w->N;
+  if (g_hooks.mock) { g_hooks.launches += 1; g_hooks.last_stream = stream; return EXL3_OK; }
+  const int err = exl3::launch_dequant(a, w->bits, stream);
+  return err ? hip_fail(err) : EXL3_OK;
+}
+
+int exl3_test_codebook(const void *states_u16, void *out_fp16, int64_t n, void *stream) {
+  if (n < 0 || (n > 0 && (!states_u16 || !out_fp16))) return EXL3_EINVAL;
+  if (n == 0) return EXL3_OK;
+  if (g_hooks.mock) { g_hooks.launches += 1; g_hooks.last_stream = stream; return EXL3_OK; }
+  const int err = exl3::launch_codebook((const uint16_t *)states_u16, (uint16_t *)out_fp16, n, stream);
+  return err ? hip_fail(err) : EXL3_OK;
+}
+
+int exl3_test_rot_in(const exl3_weight_t *w, const void *x, int64_t ldx, int64_t M, void *xr_fp16, void *stream) {
+  const int e = check_weight(w);
+  if (e != EXL3_OK) return e;
+  if (M < 0 || !xr_fp16 || !x || ldx < w->K) return EXL3_EINVAL;
+  if (M == 0) return EXL3_OK;
+  if ((uint64_t)M * w->K * 2 >= (uint64_t(1) << 31)) return EXL3_EINVAL;
+  exl3::RotArgs ra{};
+  ra.x = (const uint16_t *)x;
+  ra.ldx = ldx;
+  ra.M = (int32_t)M;
+  ra.K = (int32_t)w->K;
+  ra.n_members = 1;
+  ra.suh[0] = (const uint16_t *)w->suh;
+  ra.xr[0] = (uint16_t *)xr_fp16;
+  ra.natural_order = 1;
+  if (g_hooks.mock) { g_hooks.launches += 1; g_hooks.last_stream = stream; return EXL3_OK; }
+  const int err = exl3::launch_rot(ra, stream);
+  return err ? hip_fail(err) : EXL3_OK;
+}
+
+int exl3_test_force(int32_t m_tiles, int32_t chained, int32_t splits) {
+  if (!(m_tiles == -1 || m_tiles == 1 || m_tiles == 2 || m_tiles == 4 || m_tiles == 8)) return EXL3_EINVAL;
+  if (chained < -1 || chained > 1 || splits < 0) return EXL3_EINVAL;
+  g_hooks.m_tiles = m_tiles;
+  g_hooks.chained = chained;
+  g_hooks.splits = splits;
+  return EXL3_OK;
+}
+
+int exl3_test_mock(int32_t on) {
+  g_hooks.mock = on != 0;
+  return EXL3_OK;
+}
+
+int exl3_test_mock_counts(int64_t *launches, int64_t *fills, int64_t *fill_bytes, void **last_stream) {
+  if (launches) *launches = g_hooks.launches;
+  if (fills) *fills = g_hooks.fills;
+  if (fill_bytes) *fill_bytes = g_hooks.fill_bytes;
+  if (last_stream) *last_stream = g_hooks.last_stream;
+  g_hooks.launches = g_hooks.fills = g_hooks.fill_bytes = 0;
+  g_hooks.last_stream = nullptr;
+  return EXL3_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,69 @@
+// Internal interface between the host library (exl3_api.cpp) and the HIP
+// kernels (exl3_kernels.hip). Not installed; the public ABI is include/exl3.h.
+#pragma once
+
+#include <stdint.h>
+#include <stddef.h>
+
+namespace exl3 {
+
+constexpr int kWaves = 4;                 // waves per workgroup, every plan
+constexpr int kThreads = kWaves * 64;
+constexpr int kMaxMembers = 3;
+constexpr int kBlockCols = 128;
+constexpr int kChunk = 32;                // K depth of one MFMA (16x16x32 f16)
+
+// One member of a linear launch (a weight, a view or a group member).
+struct MemberArgs {
+  const uint8_t *words;       // first byte of this member's first block
+  const uint16_t *scales;     // fp16[N]
+  const uint16_t *svh;        // fp16[N]
+  const uint16_t *xr;         // rotated input [M][K], fp16, slot order
+  uint16_t *y;                // bf16 [M][ldy]
+  float *partials;            // [S][M][N] fp32, or null when chained
+  uint32_t *counters;         // [row_blocks][n_blocks], or null when chained
+  int64_t block_stride;       // bytes
+  int64_t ldy;                // elements
+  int32_t N;
+  int32_t n_blocks;
+  int32_t splits;             // S of the plan
+  int32_t wg_begin;           // first workgroup of this member in the grid
+};
+
+struct LinearArgs {
+  MemberArgs m[kMaxMembers];
+  int32_t n_members;
+  int32_t M;
+  int32_t K;
+  int32_t chunks;             // K / 32
+  int32_t row_blocks;         // ceil(M / (16 * m_tiles))
+  int32_t total_wgs;
+};
+
+struct RotArgs {
+  const uint16_t *x;          // bf16 [M][ldx]
+  const uint16_t *suh[kMaxMembers];
+  uint16_t *xr[kMaxMembers];  // fp16 [M][K]
+  int64_t ldx;
+  int32_t M;
+  int32_t K;
+  int32_t n_members;
+  int32_t natural_order;      // 1: natural K order (test hook), 0: MFMA slot order
+};
+
+struct DequantArgs {
+  const uint8_t *words;
+  uint16_t *out;              // fp16 [K][N]
+  int64_t block_stride;
+  int32_t K;
+  int32_t N;
+};
+
+// Launchers (exl3_kernels.hip). Each returns a hipError_t as int.
+int launch_linear(const LinearArgs &a, int bits, int m_tiles, bool chained, void *stream);
+int launch_rot(const RotArgs &a, void *stream);
+int launch_dequant(const DequantArgs &a, int bits, void *stream);
+int launch_codebook(const uint16_t *states, uint16_t *out, int64_t n, void *stream);
+int launch_fill_zero(void *ptr, size_t bytes, void *stream);
+
+}  // namespace exl3

@@ -1,0 +1,552 @@
+// HIP kernels of the EXL3 trellis-quantized linear for gfx950 (MI355X).
+//
+//   rot_kernel      Xr = fp16(FWHT128(X * suh) * 2^-4) for up to three members
+//   linear_kernel   per (row block, 128-column block, K-split group): stream the
+//                   block's packed trellis words, decode 16x16 tiles into MFMA
+//                   B operands, contract with Xr on v_mfma_f32_16x16x32_f16,
+//                   then either add the split chains in order inside the
+//                   workgroup or exchange fp32 partials through a per-block
+//                   counter whose last arriver sums them in split order and
+//                   resets it (TensorFold PR #1475, "What this changes"), and
+//                   finish with the output rotation and bf16 store
+//   dequant_kernel  test hook: the decoded weights, through the same decoder
+//   codebook_kernel test hook: the codebook on arbitrary states
+//   fill_zero       zeroes a grown counter region on the caller's stream
+//
+// Every regime (1..16 decode rows, 17..128 mid-M rows, 128-row prompt blocks),
+// every group and every column view runs the same per-output arithmetic: one
+// MFMA shape, the same K chunks per split in ascending order, the splits added
+// left to right in fp32, and one epilogue routine. A row's bits therefore do
+// not depend on the row count (PR #1467, "The arithmetic": the mid-M kernels,
+// the group launch and rot_group return the bytes of the one-weight launch).
+#include <hip/hip_runtime.h>
+
+#include "exl3_internal.h"
+
+namespace exl3 {
+namespace {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// gfx9 raw buffer resource, dword 3: 32-bit data format, no swizzle. A raw
+// load whose VGPR offset is past num_records returns zero, which pads the
+// rows beyond M with zeros without a branch.
+constexpr int kRsrcWord3 = 0x00020000;
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, kRsrcWord3);
+}
+
+// ---------------------------------------------------------------- codebook
+// cb(s) = ((40503*s + 31161) mod 2^16 AND 0x8FFF) OR 0x3000, two states per
+// 32-bit register: one packed 16-bit multiply-add and one and-or.
+constexpr unsigned short kCbMul = 40503;
+constexpr unsigned short kCbAdd = 31161;
+constexpr uint32_t kCbMask2 = 0x8FFF8FFFu;
+constexpr uint32_t kCbBase2 = 0x30003000u;
+
+__device__ __forceinline__ uint32_t codebook2(uint32_t states2) {
+  const u16x2 s = __builtin_bit_cast(u16x2, states2);
+  const u16x2 t = s * u16x2{kCbMul, kCbMul} + u16x2{kCbAdd, kCbAdd};
+  return (__builtin_bit_cast(uint32_t, t) & kCbMask2) | kCbBase2;
+}
+
+// ------------------------------------------------------------ trellis decode
+//
+// MFMA B operand of v_mfma_f32_16x16x32_f16: lane l holds 8 K values of
+// column l%16, K rows 8*(l/16) .. +7 of the 32-deep chunk. A chunk spans two
+// tile rows (kt = 2c, 2c+1); lane group g = l/16 reads tile row 2c + g/2 and
+// half h = g%2 of the column, i.e. weights i = 16*(l%16) + 8h + q, q = 0..7,
+// which are consecutive in the tile's stream (the stream walks down a column).
+// Those 8 windows start at bit 8*b*j, j = 2*(l%16) + h, and end 7b+16 bits
+// later: at most three dwords of the tile, the last ones wrapping to the
+// tile's start (tail-biting).
+//
+// Register r (r = 0..3) of the decoded operand holds window r in its low half
+// and window r+4 in its high half ("slot order"); the rotated input Xr is
+// stored in the same order, so the MFMA pairs every weight with its own input.
+
+template <int BITS>
+struct BitsTraits {
+  static constexpr int kDwords = BITS <= 4 ? 2 : 3;     // dwords a lane reads per tile
+  static constexpr int kTileBytes = 32 * BITS;
+  static constexpr int kTileDwords = 8 * BITS;
+  static constexpr bool kAligned = (BITS & 3) == 0;     // every lane's windows start at a dword
+};
+
+// Bits [P, P+32) of the 96-bit value (v2:v1:v0).
+template <int P>
+__device__ __forceinline__ uint32_t bits_at(uint32_t v0, uint32_t v1, uint32_t v2) {
+  static_assert(P >= 0 && P < 96, "window outside the lane's dwords");
+  if constexpr (P == 0) return v0;
+  else if constexpr (P < 32) return __builtin_amdgcn_alignbit(v1, v0, P);
+  else if constexpr (P == 32) return v1;
+  else if constexpr (P < 64) return __builtin_amdgcn_alignbit(v2, v1, P - 32);
+  else if constexpr (P == 64) return v2;
+  else return v2 >> (P - 64);
+}
+
+// Windows Q (low half) and Q+4 (high half) of a lane whose windows start at
+// bits 0, b, 2b, ... of (v2:v1:v0).
+template <int BITS, int Q>
+__device__ __forceinline__ uint32_t window_pair(uint32_t v0, uint32_t v1, uint32_t v2) {
+  constexpr int lo = Q * BITS;
+  constexpr int gap = 4 * BITS;
+  if constexpr (gap == 16) {
+    return bits_at<lo>(v0, v1, v2);
+  } else if constexpr (gap < 16) {
+    const uint32_t x = bits_at<lo>(v0, v1, v2);
+    const uint32_t y = x << (16 - gap);
+    return (x & 0xFFFFu) | (y & 0xFFFF0000u);
+  } else {
+    const uint32_t x = bits_at<lo>(v0, v1, v2);
+    const uint32_t y = bits_at<lo + gap - 16>(v0, v1, v2);
+    return (x & 0xFFFFu) | (y & 0xFFFF0000u);
+  }
+}
+
+// Per-lane constants of the B operand stream.
+template <int BITS>
+struct BLane {
+  uint32_t voff[BitsTraits<BITS>::kDwords];  // byte offsets of the lane's dwords in its tile row pair
+  uint32_t shift;                            // bit offset of the lane's first window in voff[0]
+};
+
+template <int BITS>
+__device__ __forceinline__ BLane<BITS> b_lane(int lane) {
+  using T = BitsTraits<BITS>;
+  BLane<BITS> r;
+  const int c = lane & 15, g = lane >> 4;
+  const int j = 2 * c + (g & 1);
+  const int bj = BITS * j;
+  const int d0 = bj >> 2;
+  r.shift = 8u * (uint32_t)(bj & 3);
+#pragma unroll
+  for (int d = 0; d < T::kDwords; ++d) {
+    int dw = d0 + d;
+    if (dw >= T::kTileDwords) dw -= T::kTileDwords;   // tail-biting wrap inside the tile
+    r.voff[d] = (uint32_t)((g >> 1) * 8 * T::kTileBytes + 4 * dw);
+  }
+  return r;
+}
+
+template <int BITS>
+__device__ __forceinline__ half8 decode8(const uint32_t (&w)[BitsTraits<BITS>::kDwords], uint32_t shift) {
+  uint32_t v0, v1, v2;
+  const uint32_t w2 = BitsTraits<BITS>::kDwords > 2 ? w[BitsTraits<BITS>::kDwords - 1] : 0u;
+  if constexpr (BitsTraits<BITS>::kAligned) {
+    v0 = w[0]; v1 = w[1]; v2 = w2;
+  } else {
+    v0 = __builtin_amdgcn_alignbit(w[1], w[0], shift);
+    v1 = __builtin_amdgcn_alignbit(w2, w[1], shift);
+    v2 = w2 >> shift;
+  }
+  u32x4 r;
+  r[0] = codebook2(window_pair<BITS, 0>(v0, v1, v2));
+  r[1] = codebook2(window_pair<BITS, 1>(v0, v1, v2));
+  r[2] = codebook2(window_pair<BITS, 2>(v0, v1, v2));
+  r[3] = codebook2(window_pair<BITS, 3>(v0, v1, v2));
+  return __builtin_bit_cast(half8, r);
+}
+
+// ------------------------------------------------------------ conversions
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t u) { return __uint_as_float((uint32_t)u << 16); }
+__device__ __forceinline__ float fp16_to_f32(uint16_t u) { return (float)__builtin_bit_cast(_Float16, u); }
+__device__ __forceinline__ uint16_t f32_to_fp16(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
+
+// fp32 -> bf16, round to nearest even; NaN stays NaN (quieted).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x0040u);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// ------------------------------------------------------------ Hadamard
+// Unnormalised 128-point Sylvester transform of one 128-vector held by a wave,
+// element `lane` in v0 and element `lane + 64` in v1. Levels h = 1, 2, ..., 64
+// in that order; each pair (i, i+h) becomes (a+b, a-b) in fp32.
+__device__ __forceinline__ void fwht128_pair(float &v0, float &v1, int lane) {
+#pragma unroll
+  for (int h = 1; h < 64; h <<= 1) {
+    const float p0 = __shfl_xor(v0, h, 64);
+    const float p1 = __shfl_xor(v1, h, 64);
+    if (lane & h) { v0 = p0 - v0; v1 = p1 - v1; }
+    else          { v0 = v0 + p0; v1 = v1 + p1; }
+  }
+  const float a = v0, b = v1;
+  v0 = a + b;
+  v1 = a - b;
+}
+
+// Epilogue of one output row of one 128-column block: scale, output Hadamard,
+// 2^-3, output signs, bf16. The one routine every regime uses.
+__device__ __forceinline__ void epilogue_row(float z0, float z1, int lane, float sc0, float sc1,
+                                             float sv0, float sv1, uint16_t *yrow) {
+  float v0 = z0 * sc0;
+  float v1 = z1 * sc1;
+  fwht128_pair(v0, v1, lane);
+  v0 = (v0 * 0.125f) * sv0;
+  v1 = (v1 * 0.125f) * sv1;
+  yrow[lane] = f32_to_bf16(v0);
+  yrow[lane + 64] = f32_to_bf16(v1);
+}
+
+// Position of logical K index k inside its 8-group in slot order:
+// logical r < 4 -> 2r, r >= 4 -> 2(r-4)+1.
+__device__ __forceinline__ int slot_pos(int k) {
+  const int r = k & 7;
+  return (k & ~7) + (r < 4 ? 2 * r : 2 * (r - 4) + 1);
+}
+
+// ------------------------------------------------------------ rot_in / rot_group
+// One wave per (member, row, 128-chunk of K).
+__global__ __launch_bounds__(kThreads) void rot_kernel(const RotArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t item = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
+  const int kc = a.K >> 7;
+  const int64_t per_member = (int64_t)a.M * kc;
+  if (item >= per_member * a.n_members) return;
+  const int j = (int)(item / per_member);
+  const int64_t rem = item - (int64_t)j * per_member;
+  const int row = (int)(rem / kc);
+  const int chunk = (int)(rem - (int64_t)row * kc);
+  const uint16_t *suh = j == 0 ? a.suh[0] : (j == 1 ? a.suh[1] : a.suh[2]);
+  uint16_t *xr = j == 0 ? a.xr[0] : (j == 1 ? a.xr[1] : a.xr[2]);
+  const int k0 = chunk * 128 + lane;
+  const int k1 = k0 + 64;
+  const uint16_t *xrow = a.x + (int64_t)row * a.ldx;
+  float v0 = bf16_to_f32(xrow[k0]) * fp16_to_f32(suh[k0]);
+  float v1 = bf16_to_f32(xrow[k1]) * fp16_to_f32(suh[k1]);
+  fwht128_pair(v0, v1, lane);
+  v0 = v0 * 0.0625f;
+  v1 = v1 * 0.0625f;
+  uint16_t *xrrow = xr + (int64_t)row * a.K;
+  xrrow[a.natural_order ? k0 : slot_pos(k0)] = f32_to_fp16(v0);
+  xrrow[a.natural_order ? k1 : slot_pos(k1)] = f32_to_fp16(v1);
+}
+
+// ------------------------------------------------------------ linear
+
+template <int MT>
+struct Depth { static constexpr int P = MT == 1 ? 4 : (MT == 2 ? 3 : 2); };   // chunks in flight
+
+template <int BITS, int MT>
+struct Stage {
+  u32x4 a[MT];
+  uint32_t b[2][BitsTraits<BITS>::kDwords];
+};
+
+template <int BITS, int MT>
+__device__ __forceinline__ void load_stage(Stage<BITS, MT> &st, __amdgpu_buffer_rsrc_t ra,
+                                           __amdgpu_buffer_rsrc_t rb, const uint32_t (&voff_a)[MT],
+                                           const uint32_t (&voff_b)[2][BitsTraits<BITS>::kDwords],
+                                           int chunk) {
+  const int soff_a = chunk * 64;                 // 32 fp16 per row per chunk
+  const int soff_b = chunk * 512 * BITS;         // two tile rows of 8 tiles
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+    st.a[mt] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, (int)voff_a[mt], soff_a, 0));
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int d = 0; d < BitsTraits<BITS>::kDwords; ++d)
+      st.b[i][d] = __builtin_amdgcn_raw_buffer_load_b32(rb, (int)voff_b[i][d], soff_b, 0);
+}
+
+template <int BITS, int MT>
+__device__ __forceinline__ void compute_stage(const Stage<BITS, MT> &st, uint32_t shift, f32x4 (&acc)[MT][2]) {
+  half8 bf[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) bf[i] = decode8<BITS>(st.b[i], shift);
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const half8 af = __builtin_bit_cast(half8, st.a[mt]);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      acc[mt][i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf[i], acc[mt][i], 0, 0, 0);
+  }
+}
+
+// One K-split chain: chunks [c0, c1) in ascending order, from zero.
+template <int BITS, int MT>
+__device__ __forceinline__ void run_chain(f32x4 (&acc)[MT][2], __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
+                                          const uint32_t (&voff_a)[MT],
+                                          const uint32_t (&voff_b)[2][BitsTraits<BITS>::kDwords],
+                                          uint32_t shift, int c0, int c1) {
+  constexpr int P = Depth<MT>::P;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int i = 0; i < 2; ++i) acc[mt][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  Stage<BITS, MT> st[P];
+#pragma unroll
+  for (int p = 0; p < P; ++p)
+    if (c0 + p < c1) load_stage<BITS, MT>(st[p], ra, rb, voff_a, voff_b, c0 + p);
+  for (int c = c0; c < c1; c += P) {
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      if (c + p < c1) {
+        compute_stage<BITS, MT>(st[p], shift, acc);
+        if (c + p + P < c1) load_stage<BITS, MT>(st[p], ra, rb, voff_a, voff_b, c + p + P);
+      }
+    }
+  }
+}
+
+template <int BITS, int MT, bool CHAINED>
+__global__ __launch_bounds__(kThreads) void linear_kernel(const LinearArgs a) {
+  using T = BitsTraits<BITS>;
+  constexpr int R = 16 * MT;                      // rows per workgroup
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int bid = blockIdx.x;
+
+  // member of this workgroup (uniform)
+  int j = 0;
+  if (a.n_members > 1 && bid >= a.m[1].wg_begin) j = 1;
+  if (a.n_members > 2 && bid >= a.m[2].wg_begin) j = 2;
+  const MemberArgs &m = a.m[j];
+  const int S = m.splits;
+  const int groups = CHAINED ? 1 : S;             // workgroups per (row block, column block)
+  const int local = bid - m.wg_begin;
+  const int per_rb = m.n_blocks * groups;
+  const int rb = local / per_rb;
+  const int rem = local - rb * per_rb;
+  const int nb = rem / groups;
+  const int sg = rem - nb * groups;
+  const int s_begin = CHAINED ? 0 : sg;
+  const int s_end = CHAINED ? S : sg + 1;
+  const int M = a.M, K = a.K, C = a.chunks;
+  const int row_base = rb * R;
+  const int col0 = nb * kBlockCols;
+
+  // buffer resources: this member's rotated input, this block's words
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(m.xr, (uint32_t)((uint64_t)M * K * 2));
+  const __amdgpu_buffer_rsrc_t rbuf = make_rsrc(m.words + (int64_t)nb * m.block_stride, (uint32_t)(16u * K * BITS));
+
+  const int c = lane & 15, g = lane >> 4;
+  uint32_t voff_a[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int row = row_base + 16 * mt + c;
+    voff_a[mt] = row < M ? (uint32_t)(row * 2 * K + 16 * g) : kOutOfRange;
+  }
+  const BLane<BITS> bl = b_lane<BITS>(lane);
+  uint32_t voff_b[2][T::kDwords];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int d = 0; d < T::kDwords; ++d) voff_b[i][d] = bl.voff[d] + (uint32_t)((2 * wave + i) * T::kTileBytes);
+
+  f32x4 acc[MT][2];
+  f32x4 z[CHAINED ? MT : 1][2];
+  for (int s = s_begin; s < s_end; ++s) {
+    const int c0 = (int)(((int64_t)s * C) / S);
+    const int c1 = (int)(((int64_t)(s + 1) * C) / S);
+    run_chain<BITS, MT>(acc, ra, rbuf, voff_a, voff_b, bl.shift, c0, c1);
+    if constexpr (CHAINED) {
+      // splits added left to right: ((P0 + P1) + P2) + ...
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 2; ++i) z[mt][i] = (s == 0) ? acc[mt][i] : z[mt][i] + acc[mt][i];
+    }
+  }
+
+  const float sc0 = fp16_to_f32(m.scales[col0 + lane]);
+  const float sc1 = fp16_to_f32(m.scales[col0 + lane + 64]);
+  const float sv0 = fp16_to_f32(m.svh[col0 + lane]);
+  const float sv1 = fp16_to_f32(m.svh[col0 + lane + 64]);
+
+  if constexpr (CHAINED) {
+    __shared__ float zbuf[16][132];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int row0 = row_base + 16 * mt;
+      if (row0 >= M) break;                         // uniform
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) zbuf[4 * g + r][16 * (2 * wave + i) + c] = z[mt][i][r];
+      __syncthreads();
+      for (int rr = wave; rr < 16; rr += kWaves) {
+        const int row = row0 + rr;
+        if (row < M)
+          epilogue_row(zbuf[rr][lane], zbuf[rr][lane + 64], lane, sc0, sc1, sv0, sv1,
+                       m.y + (int64_t)row * m.ldy + col0);
+      }
+    }
+  } else {
+    // write this split's fp32 partial P_s[row][col]
+    const int N = m.N;
+    float *P = m.partials + (int64_t)s_begin * M * N + col0;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = row_base + 16 * mt + 4 * g + r;
+          if (row < M) P[(int64_t)row * N + 16 * (2 * wave + i) + c] = acc[mt][i][r];
+        }
+    // publish: every wave's stores reach memory before the counter moves
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __syncthreads();
+    __shared__ int s_last;
+    uint32_t *counter = m.counters + (int64_t)rb * m.n_blocks + nb;
+    if (threadIdx.x == 0) {
+      const uint32_t prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_last = prev == (uint32_t)(S - 1);
+    }
+    __syncthreads();
+    if (!s_last) return;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    // the last arriver resets the counter it consumed: zero at rest
+    if (threadIdx.x == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const float *P0 = m.partials + col0;
+    const int64_t split_stride = (int64_t)M * N;
+    for (int rr = wave; rr < R; rr += kWaves) {
+      const int row = row_base + rr;
+      if (row >= M) break;
+      const float *p = P0 + (int64_t)row * N;
+      float z0 = p[lane], z1 = p[lane + 64];
+      for (int s = 1; s < S; ++s) {
+        p += split_stride;
+        z0 = z0 + p[lane];
+        z1 = z1 + p[lane + 64];
+      }
+      epilogue_row(z0, z1, lane, sc0, sc1, sv0, sv1, m.y + (int64_t)row * m.ldy + col0);
+    }
+  }
+}
+
+// ------------------------------------------------------------ test hooks
+
+template <int BITS>
+__global__ __launch_bounds__(kThreads) void dequant_kernel(const DequantArgs a) {
+  using T = BitsTraits<BITS>;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int C = a.K / kChunk;
+  const int nb = blockIdx.x / C;
+  const int chunk = blockIdx.x - nb * C;
+  const __amdgpu_buffer_rsrc_t rbuf = make_rsrc(a.words + (int64_t)nb * a.block_stride, (uint32_t)(16u * a.K * BITS));
+  const BLane<BITS> bl = b_lane<BITS>(lane);
+  const int c = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    uint32_t w[T::kDwords];
+#pragma unroll
+    for (int d = 0; d < T::kDwords; ++d)
+      w[d] = __builtin_amdgcn_raw_buffer_load_b32(rbuf, (int)(bl.voff[d] + (2 * wave + i) * T::kTileBytes),
+                                                  chunk * 512 * BITS, 0);
+    const u32x4 v = __builtin_bit_cast(u32x4, decode8<BITS>(w, bl.shift));
+    const int kbase = 16 * (2 * chunk + (g >> 1)) + 8 * (g & 1);
+    const int n = nb * kBlockCols + 16 * (2 * wave + i) + c;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      a.out[(int64_t)(kbase + r) * a.N + n] = (uint16_t)(v[r] & 0xFFFFu);
+      a.out[(int64_t)(kbase + r + 4) * a.N + n] = (uint16_t)(v[r] >> 16);
+    }
+  }
+}
+
+__global__ void codebook_kernel(const uint16_t *states, uint16_t *out, int64_t n) {
+  const int64_t pair = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t i0 = 2 * pair;
+  if (i0 >= n) return;
+  const uint32_t s0 = states[i0];
+  const uint32_t s1 = (i0 + 1 < n) ? states[i0 + 1] : 0u;
+  const uint32_t w = codebook2(s0 | (s1 << 16));
+  out[i0] = (uint16_t)(w & 0xFFFFu);
+  if (i0 + 1 < n) out[i0 + 1] = (uint16_t)(w >> 16);
+}
+
+__global__ void fill_zero_kernel(uint32_t *p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = 0u;
+}
+
+// ------------------------------------------------------------ dispatch tables
+
+typedef void (*LinearFn)(const LinearArgs);
+
+template <int BITS, bool CHAINED>
+constexpr LinearFn pick_mt(int mti) {
+  return mti == 0 ? linear_kernel<BITS, 1, CHAINED>
+       : mti == 1 ? linear_kernel<BITS, 2, CHAINED>
+       : mti == 2 ? linear_kernel<BITS, 4, CHAINED>
+                  : linear_kernel<BITS, 8, CHAINED>;
+}
+
+template <int BITS>
+LinearFn pick_linear(int mti, bool chained) {
+  return chained ? pick_mt<BITS, true>(mti) : pick_mt<BITS, false>(mti);
+}
+
+}  // namespace
+
+int launch_linear(const LinearArgs &a, int bits, int m_tiles, bool chained, void *stream) {
+  const int mti = m_tiles == 1 ? 0 : m_tiles == 2 ? 1 : m_tiles == 4 ? 2 : 3;
+  LinearFn fn = nullptr;
+  switch (bits) {
+    case 2: fn = pick_linear<2>(mti, chained); break;
+    case 3: fn = pick_linear<3>(mti, chained); break;
+    case 4: fn = pick_linear<4>(mti, chained); break;
+    case 5: fn = pick_linear<5>(mti, chained); break;
+    case 6: fn = pick_linear<6>(mti, chained); break;
+    case 7: fn = pick_linear<7>(mti, chained); break;
+    case 8: fn = pick_linear<8>(mti, chained); break;
+    default: return (int)hipErrorInvalidValue;
+  }
+  hipLaunchKernelGGL(fn, dim3((unsigned)a.total_wgs), dim3(kThreads), 0, (hipStream_t)stream, a);
+  return (int)hipGetLastError();
+}
+
+int launch_rot(const RotArgs &a, void *stream) {
+  const int64_t items = (int64_t)a.n_members * a.M * (a.K / 128);
+  const int64_t wgs = (items + kWaves - 1) / kWaves;
+  hipLaunchKernelGGL(rot_kernel, dim3((unsigned)wgs), dim3(kThreads), 0, (hipStream_t)stream, a);
+  return (int)hipGetLastError();
+}
+
+int launch_dequant(const DequantArgs &a, int bits, void *stream) {
+  const unsigned wgs = (unsigned)((a.N / kBlockCols) * (a.K / kChunk));
+  const dim3 grid(wgs), block(kThreads);
+  hipStream_t s = (hipStream_t)stream;
+  switch (bits) {
+    case 2: hipLaunchKernelGGL(dequant_kernel<2>, grid, block, 0, s, a); break;
+    case 3: hipLaunchKernelGGL(dequant_kernel<3>, grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL(dequant_kernel<4>, grid, block, 0, s, a); break;
+    case 5: hipLaunchKernelGGL(dequant_kernel<5>, grid, block, 0, s, a); break;
+    case 6: hipLaunchKernelGGL(dequant_kernel<6>, grid, block, 0, s, a); break;
+    case 7: hipLaunchKernelGGL(dequant_kernel<7>, grid, block, 0, s, a); break;
+    case 8: hipLaunchKernelGGL(dequant_kernel<8>, grid, block, 0, s, a); break;
+    default: return (int)hipErrorInvalidValue;
+  }
+  return (int)hipGetLastError();
+}
+
+int launch_codebook(const uint16_t *states, uint16_t *out, int64_t n, void *stream) {
+  const int64_t pairs = (n + 1) / 2;
+  const unsigned wgs = (unsigned)((pairs + 255) / 256);
+  hipLaunchKernelGGL(codebook_kernel, dim3(wgs), dim3(256), 0, (hipStream_t)stream, states, out, n);
+  return (int)hipGetLastError();
+}
+
+int launch_fill_zero(void *ptr, size_t bytes, void *stream) {
+  const int64_t n = (int64_t)(bytes / 4);
+  if (n == 0) return 0;
+  int64_t wgs = (n + 255) / 256;
+  if (wgs > 4096) wgs = 4096;
+  hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)wgs), dim3(256), 0, (hipStream_t)stream, (uint32_t *)ptr, n);
+  return (int)hipGetLastError();
+}
+
+}  // namespace exl3
