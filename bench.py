@@ -1,0 +1,346 @@
+#!/usr/bin/env python3
+"""Benchmark of the EXL3 linear on one MI355X.
+
+A step is one pass of the whole hot path over one batch: for the 27B
+decode-row grouped linear (K = 5120, 4 bits, M = 16) it is the {q, k, v}
+group and the {gate, up} group, each as one rotation launch and one linear
+launch (trellis decode + MFMA contraction + split-K exchange + epilogue).
+Steps cycle through 8 distinct copies of the weights (8 x 110 MB) so each
+step streams its weights from HBM rather than from the 256 MB last-level
+cache. The timed steps replay HIP graphs of the step (the library's calls
+allocate and memset nothing, so they capture), bracketed by a device
+synchronisation on both sides.
+
+Printed: one JSON line with the weight-stream GB/s of the step (`value`),
+the roofline of the dominant kernel (the {gate, up} linear launch, timed with
+HIP events around graph replays of back-to-back launches on its stream), the
+CPU oracle on a bounded sample, and extra figures: the same group at M = 1
+and 7, the 3.5 bpw MLP at M = 128 (TFLOP/s), one layer's 8192-row prefill
+(TFLOP/s) and the 6-bit head and its span views at M = 16 (GB/s).
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "EXL3 linear weight-stream GB/s at M=1..16; TFLOP/s at M=128 and 8192-row prefill"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA
+NCOPY = 8
+KERNEL_SRC = os.path.join(ROOT, "trellis_quantized_linear_amd", "csrc", "exl3_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_linear_gate_up_m16.json")
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def alg_bytes(weights, M, with_x=True):
+    """Algorithmic bytes of one group call: packed words, fp16 scales, suh and
+    svh per member, bf16 X once, bf16 Y per member."""
+    K = weights[0].K
+    b = 2 * M * K if with_x else 0
+    for w in weights:
+        b += w.K * w.N * w.bits // 8 + 2 * w.N + 2 * w.K + 2 * w.N + 2 * M * w.N
+    return b
+
+
+def flops(weights, M):
+    return sum(2 * M * w.K * w.N for w in weights)
+
+
+class Group:
+    """One group call's device state: members, input, outputs, workspace."""
+
+    def __init__(self, ex, weights, x, M, ws):
+        import torch
+        self.ex, self.w, self.x, self.M, self.ws = ex, weights, x, M, ws
+        self.y = [torch.empty((M, w.N), dtype=torch.bfloat16, device="cuda") for w in weights]
+
+    def rotate(self):
+        self.ex.exl3_rotate(self.w, self.x, self.ws, M=self.M)
+
+    def linear(self):
+        self.ex.exl3_linear_rotated(self.w, self.y, self.ws, self.M)
+
+    def call(self):
+        self.rotate()
+        self.linear()
+
+
+def capture(fn):
+    import torch
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()                      # warm once outside capture on the same stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def time_events(fn, reps):
+    """Average ms per fn() call, HIP events on the current stream."""
+    import torch
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(st)
+    for _ in range(reps):
+        fn()
+    e1.record(st)
+    e1.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def upload_copies(ex, layers, n):
+    return [[ex.Weight.from_host(L, "cuda") for L in layers] for _ in range(n)]
+
+
+def x_dev(M, K, sigma, tag):
+    import numpy as np
+    import torch
+    from trellis_quantized_linear_amd import synth
+    x = synth.gen_x(synth.rng_for("bench", tag, M, K), M, K, sigma)
+    return torch.from_numpy(x.view(np.int16).copy()).to("cuda").view(torch.bfloat16)
+
+
+def cpu_baseline(layers_kv, M):
+    """The oracle as it stands, one thread, on the k and v members of the
+    {q, k, v} group at M rows: decode + rotations + float64 contraction."""
+    from threadpoolctl import threadpool_limits
+    from oracle import exl3_oracle as O
+    from trellis_quantized_linear_amd import synth
+    x = synth.gen_x(synth.rng_for("bench", "x", M, 5120), M, 5120)
+    nbytes = 2 * M * 5120
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        for L in layers_kv:
+            O.linear_packed(L.words, L.K, L.N, L.bits, L.scales, L.suh, L.svh, x)
+            nbytes += L.K * L.N * L.bits // 8 + 4 * L.N + 2 * L.K + 2 * M * L.N
+        dt = time.perf_counter() - t0
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"k and v members of the q/k/v group (16 of the step's 336 column blocks, "
+                      f"{nbytes / 1e6:.1f} MB algorithmic), M={M}, numpy float64 oracle, {dt:.1f} s"}
+
+
+def traffic_record():
+    """HBM traffic per launch of the dominant kernel from the committed PMC
+    summary, if it was taken on the current kernel source; else None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    rec = json.load(open(TRAFFIC_FILE))
+    cur = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+    return rec.get("bytes_per_launch") if rec.get("kernel_sha256") == cur else None
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-extra", action="store_true", help="skip the M=128, prefill and head figures")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run one plain 1 GiB device copy (PMC scale reference)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import trellis_quantized_linear_amd.exl3 as ex
+    from trellis_quantized_linear_amd import synth
+
+    ex.lib()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    K, bits, M = synth.HIDDEN, 4, 16
+    names = [("q", synth.Q_COLS), ("k", synth.KV_COLS), ("v", synth.KV_COLS),
+             ("gate", synth.INTERMEDIATE), ("up", synth.INTERMEDIATE)]
+    layers = {n: synth.gen_layer("bench-27b", n, K, N, bits) for n, N in names}
+    log("uploading", NCOPY, "copies of q/k/v/gate/up")
+    copies = upload_copies(ex, [layers[n] for n, _ in names], NCOPY)
+    x = x_dev(M, K, 1.0, "x")
+    ws_qkv = ex.Workspace().reserve(copies[0][:3], 128)
+    ws_gu = ex.Workspace().reserve(copies[0][3:], 128)
+    torch.cuda.synchronize()
+
+    def step_groups(c, m=M, xx=x):
+        return Group(ex, copies[c][:3], xx, m, ws_qkv), Group(ex, copies[c][3:], xx, m, ws_gu)
+
+    # eager reference, then one graph per weight copy
+    steps = [step_groups(c) for c in range(NCOPY)]
+    for g1, g2 in steps:
+        g1.call()
+        g2.call()
+    torch.cuda.synchronize()
+    ref = [[y.clone() for y in g1.y + g2.y] for g1, g2 in steps]
+    graphs = [capture(lambda g1=g1, g2=g2: (g1.call(), g2.call())) for g1, g2 in steps]
+    for c, gr in enumerate(graphs):
+        gr.replay()
+        torch.cuda.synchronize()
+        got = steps[c][0].y + steps[c][1].y
+        assert all(torch.equal(a.view(torch.int16), b.view(torch.int16)) for a, b in zip(got, ref[c])), \
+            "graph replay differs from the eager call"
+
+    for i in range(args.warmup):
+        graphs[i % NCOPY].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        graphs[i % NCOPY].replay()
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    ms_step = dt * 1e3 / args.steps
+    step_bytes = alg_bytes(copies[0][:3], M) + alg_bytes(copies[0][3:], M)
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+    log(f"step {ms_step * 1e3:.2f} us, {step_bytes / 1e6:.2f} MB -> {value:.1f} GB/s")
+
+    # dominant kernel: the {gate, up} linear launch, back-to-back over the copies
+    gu = [s[1] for s in steps]
+    for g in gu:
+        g.rotate()
+    torch.cuda.synchronize()
+    reps_in_graph = 2
+    g_lin = capture(lambda: [g.linear() for _ in range(reps_in_graph) for g in gu])
+    launches = reps_in_graph * NCOPY
+    ms_graph = time_events(g_lin.replay, 20)
+    ms_kernel = ms_graph / launches
+    kbytes = alg_bytes(copies[0][3:], M)
+    achieved = kbytes / (ms_kernel * 1e-3) / 1e9
+    log(f"gate/up linear: {ms_kernel * 1e3:.2f} us per launch -> {achieved:.1f} GB/s")
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_record(),
+                "kernel": "linear_kernel<bits=4, m_tiles=1> of the {gate, up} group, M=16",
+                "alg_bytes_per_launch": kbytes, "us_per_launch": round(ms_kernel * 1e3, 3)}
+
+    extra = {}
+    if not args.no_extra:
+        extra = run_extras(ex, torch, synth, layers, copies)
+
+    cpu = None
+    if not args.no_cpu:
+        log("CPU oracle baseline (k, v at M=16, one thread)")
+        cpu = cpu_baseline([layers["k"], layers["v"]], M)
+
+    if args.calibrate_copy:
+        # an elementwise kernel that reads 1 GiB and writes 1 GiB
+        a = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        torch.mul(a, 1.0, out=b)
+        torch.cuda.synchronize()
+        extra["copy_calibration_bytes"] = {"read": 1 << 30, "write": 1 << 30}
+
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+        "config": {"workload": "27B decode-row grouped linear: {q,k,v} and {gate,up} groups, K=5120, 4 bits, "
+                               "M=16, X bf16 ~N(0,1)",
+                   "K": K, "bits": bits, "M": M, "members": {n: N for n, N in names},
+                   "weight_copies": NCOPY, "step_alg_bytes": step_bytes},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def run_extras(ex, torch, synth, layers, copies):
+    extra = {}
+    K = synth.HIDDEN
+    # the same grouped step at M = 1 and 7 (graph replays over the copies)
+    for m in (1, 7):
+        xx = x_dev(m, K, 1.0, f"x{m}")
+        wsa = ex.Workspace().reserve(copies[0][:3], m)
+        wsb = ex.Workspace().reserve(copies[0][3:], m)
+        gs = [(Group(ex, c[:3], xx, m, wsa), Group(ex, c[3:], xx, m, wsb)) for c in copies]
+        graphs = [capture(lambda a=a, b=b: (a.call(), b.call())) for a, b in gs]
+        ms = time_events(lambda: [g.replay() for g in graphs], 10) / len(graphs)
+        by = alg_bytes(copies[0][:3], m) + alg_bytes(copies[0][3:], m)
+        extra[f"decode_step_M{m}_GBps"] = round(by / (ms * 1e-3) / 1e9, 1)
+        log(f"decode step M={m}: {ms * 1e3:.2f} us, {extra[f'decode_step_M{m}_GBps']} GB/s")
+
+    # 27B dense SwiGLU MLP at 3.5 bpw, M = 128: {gate, up} 3-bit group + down 4-bit
+    m = 128
+    mlp = [synth.gen_layer("bench-mlp", "gate", K, synth.INTERMEDIATE, 3),
+           synth.gen_layer("bench-mlp", "up", K, synth.INTERMEDIATE, 3),
+           synth.gen_layer("bench-mlp", "down", synth.INTERMEDIATE, K, 4)]
+    mc = upload_copies(ex, mlp, 4)
+    xa = x_dev(m, K, 1.0, "mlp-x")
+    xb = x_dev(m, synth.INTERMEDIATE, 1.0, "mlp-x2")
+    wsa = ex.Workspace().reserve(mc[0][:2], m)
+    wsb = ex.Workspace().reserve(mc[0][2:], m)
+    gs = [(Group(ex, c[:2], xa, m, wsa), Group(ex, c[2:], xb, m, wsb)) for c in mc]
+    graphs = [capture(lambda a=a, b=b: (a.call(), b.call())) for a, b in gs]
+    ms = time_events(lambda: [g.replay() for g in graphs], 10) / len(graphs)
+    fl = flops(mc[0], m)
+    by = alg_bytes(mc[0][:2], m) + alg_bytes(mc[0][2:], m)
+    extra["mlp_M128_TFLOPs"] = round(fl / (ms * 1e-3) / 1e12, 1)
+    extra["mlp_M128_us"] = round(ms * 1e3, 2)
+    extra["mlp_M128_frac_mfma"] = round(fl / (ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)
+    extra["mlp_M128_GBps"] = round(by / (ms * 1e-3) / 1e9, 1)
+    log(f"MLP M=128: {ms * 1e3:.1f} us, {extra['mlp_M128_TFLOPs']} TFLOP/s")
+    del gs, graphs, mc
+
+    # one 27B layer's six linears over an 8192-row prompt (4 bits, X ~ N(0, 0.5))
+    m = 8192
+    six = [copies[0][0], copies[0][1], copies[0][2], copies[0][3], copies[0][4]]
+    down = ex.Weight.from_host(synth.gen_layer("bench-27b", "down", synth.INTERMEDIATE, K, 4), "cuda")
+    xa = x_dev(m, K, 0.5, "prefill-x")
+    xb = x_dev(m, synth.INTERMEDIATE, 0.5, "prefill-x2")
+    wsa = ex.Workspace().reserve(six[:3], m)
+    wsb = ex.Workspace().reserve(six[3:], m)
+    wsc = ex.Workspace().reserve([down], m)
+    ga, gb, gc = Group(ex, six[:3], xa, m, wsa), Group(ex, six[3:], xa, m, wsb), Group(ex, [down], xb, m, wsc)
+    fn = lambda: (ga.call(), gb.call(), gc.call())
+    fn()
+    ms = time_events(fn, 3)
+    fl = flops(six + [down], m)
+    extra["prefill_8192_TFLOPs"] = round(fl / (ms * 1e-3) / 1e12, 1)
+    extra["prefill_8192_ms_per_layer"] = round(ms, 3)
+    extra["prefill_8192_frac_mfma"] = round(fl / (ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)
+    log(f"prefill 8192 rows: {ms:.2f} ms per layer, {extra['prefill_8192_TFLOPs']} TFLOP/s")
+    del ga, gb, gc, xa, xb, wsa, wsb, wsc
+
+    # the 6-bit head 5120 -> 248,320 and its span views, M = 16
+    m = 16
+    head = ex.Weight.from_host(synth.gen_layer("bench-head", "head", K, synth.VOCAB, 6), "cuda")
+    xx = x_dev(m, K, 1.0, "head-x")
+    for tag, w in (("head_full", head), ("head_span_A", head.columns(0, 98304))):
+        ws = ex.Workspace().reserve([w], m)
+        g = Group(ex, [w], xx, m, ws)
+        gr = capture(g.call)
+        ms = time_events(gr.replay, 10)
+        extra[f"{tag}_M16_GBps"] = round(alg_bytes([w], m) / (ms * 1e-3) / 1e9, 1)
+        extra[f"{tag}_M16_us"] = round(ms * 1e3, 2)
+        log(f"{tag}: {ms * 1e3:.1f} us, {extra[f'{tag}_M16_GBps']} GB/s")
+    # span B is 64 blocks (31.5 MB): cycle 16 distinct 64-block views of the
+    # head (504 MB) so it streams from HBM, not from the last-level cache
+    views = [head.columns(240128 - 128 * 64 * i, 8192) for i in range(16)]
+    ws = ex.Workspace().reserve([views[0]], m)
+    gs = [Group(ex, [v], xx, m, ws) for v in views]
+    gr = capture(lambda: [g.call() for g in gs])
+    ms = time_events(gr.replay, 10) / len(gs)
+    extra["head_span_B_M16_GBps"] = round(alg_bytes([views[0]], m) / (ms * 1e-3) / 1e9, 1)
+    extra["head_span_B_M16_us"] = round(ms * 1e3, 2)
+    log(f"head_span_B: {ms * 1e3:.1f} us, {extra['head_span_B_M16_GBps']} GB/s")
+    return extra
+
+
+if __name__ == "__main__":
+    main()

@@ -160,6 +160,20 @@ int exl3_linear_group(int32_t n_members, const exl3_weight_t *const *w, const vo
                       int64_t ldx, int64_t M, void *const *y, const int64_t *ldy,
                       const exl3_workspace_t *ws, void *stream);
 
+/* exl3_rotate / exl3_linear_rotated — the two launches of exl3_linear_group,
+ * callable one at a time (the pages keep the rotation, rot_in / rot_group,
+ * and the linear as separate launches: PR #1467, "What this changes").
+ * exl3_rotate writes the members' rotated inputs into the workspace;
+ * exl3_linear_rotated then runs the linear on what the workspace holds. The
+ * second call must name the same members and M as the exl3_rotate before it
+ * on the same workspace (and stream); otherwise its output is meaningless
+ * (it still stays inside the workspace and y). Together they produce exactly
+ * the bytes of exl3_linear_group. Errors: as exl3_linear_group. */
+int exl3_rotate(int32_t n_members, const exl3_weight_t *const *w, const void *x, int64_t ldx, int64_t M,
+                const exl3_workspace_t *ws, void *stream);
+int exl3_linear_rotated(int32_t n_members, const exl3_weight_t *const *w, int64_t M, void *const *y,
+                        const int64_t *ldy, const exl3_workspace_t *ws, void *stream);
+
 /* exl3_strerror — static text for an error code. */
 const char *exl3_strerror(int code);
 

@@ -43,7 +43,7 @@ def fake_weight(K, N, bits, base=0x10000000, block_stride=None):
 def test_exports_every_declared_symbol(lib):
     text = open(ex.HEADER).read()
     names = sorted(set(re.findall(r"^\s*(?:int|const char \*)\s*(exl3_\w+)\s*\(", text, re.M)))
-    assert len(names) == 15
+    assert len(names) == 17
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(ex._SIGNATURES), set(names) ^ set(ex._SIGNATURES)
@@ -222,17 +222,22 @@ def test_workspace_too_small_is_refused(lib):
 
 
 def test_workspace_for_max_rows_covers_smaller_calls(lib):
+    """A workspace of exactly the size exl3_workspace_need reports for
+    max_rows accepts every call of 1..max_rows rows, across the regime
+    boundaries (decode, mid-M, prompt)."""
     ex.exl3_test_mock(True)
-    shapes = [(5120, 1024), (5120, 6144), (5120, 17408), (17408, 5120), (5120, 248320)]
+    shapes = [(5120, 1024), (5120, 6144), (5120, 17408), (17408, 5120), (5120, 248320), (256, 256)]
     for K, N in shapes:
         w = fake_weight(K, N, 4)
         for max_rows in (16, 100, 128, 300, 8192):
             need, cb = ex.exl3_workspace_need([w], max_rows)
+            ws = ex.exl3_workspace_t(0x20000000, need, cb)
             for M in sorted({1, 7, 16, 17, 33, 64, 100, 128, 129, 256, max_rows}):
                 if M > max_rows:
                     continue
-                n2, c2 = ex.exl3_workspace_need([w], M)
-                assert n2 <= need and c2 <= cb, (K, N, max_rows, M)
+                rc = lib.exl3_linear(ctypes.byref(w.desc), 0x30000000, K, M, 0x40000000, N, ctypes.byref(ws), None)
+                assert rc == 0, (K, N, max_rows, M, rc)
+    ex.exl3_test_mock_counts()
 
 
 def test_workspace_grow_errors(lib):
@@ -242,6 +247,26 @@ def test_workspace_grow_errors(lib):
     assert lib.exl3_workspace_grow(ctypes.byref(ws), 0x20000000, 256, 512, None) == ex.EXL3_EWORKSPACE
     assert lib.exl3_workspace_grow(None, 0x20000000, 1024, 256, None) == ex.EXL3_EINVAL
     assert lib.exl3_workspace_grow(ctypes.byref(ws), None, 1024, 256, None) == ex.EXL3_EINVAL
+
+
+def test_rotate_and_linear_rotated_are_one_launch_each(lib):
+    ex.exl3_test_mock(True)
+    a = fake_weight(5120, 6144, 4)
+    b = fake_weight(5120, 1024, 4, base=0x50000000)
+    need, cb = ex.exl3_workspace_need([a, b], 16)
+    ws = ex.exl3_workspace_t(0x20000000, need, cb)
+    arr = ex._wlist([a, b])
+    ys = (ctypes.c_void_p * 2)(0x80000000, 0x90000000)
+    ld = (ctypes.c_int64 * 2)(6144, 1024)
+    assert lib.exl3_rotate(2, arr, 0x30000000, 5120, 16, ctypes.byref(ws), 0x777000) == 0
+    assert ex.exl3_test_mock_counts()[0] == 1
+    assert lib.exl3_linear_rotated(2, arr, 16, ys, ld, ctypes.byref(ws), 0x777000) == 0
+    launches, fills, _, s = ex.exl3_test_mock_counts()
+    assert (launches, fills, s) == (1, 0, 0x777000)
+    # each phase checks only what it uses
+    assert lib.exl3_rotate(2, arr, None, 5120, 16, ctypes.byref(ws), None) == ex.EXL3_EINVAL
+    assert lib.exl3_linear_rotated(2, arr, 16, None, ld, ctypes.byref(ws), None) == ex.EXL3_EINVAL
+    assert lib.exl3_linear_rotated(2, arr, 16, ys, ld, None, None) == ex.EXL3_EWORKSPACE
 
 
 def test_strerror_covers_every_code(lib):

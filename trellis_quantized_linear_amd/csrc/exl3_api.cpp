@@ -144,12 +144,12 @@ int check_group(int32_t n, const exl3_weight_t *const *w, int64_t M, MemberPlan 
   return EXL3_OK;
 }
 
-void fill_need(const MemberPlan *mp, int n, int64_t M, size_t *bytes, size_t *counter_bytes) {
+// Sizes of one call at M rows: the counter region and what follows it.
+void call_need(const MemberPlan *mp, int n, int64_t M, size_t *rest, size_t *counter_bytes) {
   const Launch L = choose_launch(mp, n, M);
   const Layout lay = layout_for(mp, n, M, mp[0].w->K, L);
-  const size_t cb = align_up(lay.counters * 4);
-  if (counter_bytes) *counter_bytes = std::max(*counter_bytes, cb);
-  if (bytes) *bytes = std::max(*bytes, cb + lay.rest);
+  *counter_bytes = std::max(*counter_bytes, align_up(lay.counters * 4));
+  *rest = std::max(*rest, lay.rest);
 }
 
 int issue_fill(void *ptr, size_t bytes, void *stream) {
@@ -200,14 +200,15 @@ int exl3_workspace_need(int32_t n_members, const exl3_weight_t *const *w, int64_
   MemberPlan mp[kMaxMembers];
   const int e = check_group(n_members, w, M, mp);
   if (e != EXL3_OK) return e;
-  *bytes = 0;
-  *counter_bytes = 0;
+  size_t rest = 0, cb = 0;
   // sizes grow with M inside each regime; the regime boundaries and M itself
-  // bound every smaller call
+  // bound every smaller call. The counter region sits at a fixed offset, so
+  // the largest counter need and the largest rest add up.
   const int64_t probes[3] = {std::min<int64_t>(M, 16), std::min<int64_t>(M, 128), M};
   for (int64_t p : probes)
-    if (p > 0) fill_need(mp, n_members, p, bytes, counter_bytes);
-  if (*bytes < *counter_bytes) *bytes = *counter_bytes;
+    if (p > 0) call_need(mp, n_members, p, &rest, &cb);
+  *counter_bytes = cb;
+  *bytes = cb + rest;
   return EXL3_OK;
 }
 
@@ -229,18 +230,31 @@ int exl3_workspace_reset(const exl3_workspace_t *ws, void *stream) {
   return issue_fill(ws->ptr, ws->counter_bytes, stream);
 }
 
-int exl3_linear_group(int32_t n_members, const exl3_weight_t *const *w, const void *x, int64_t ldx, int64_t M,
-                      void *const *y, const int64_t *ldy, const exl3_workspace_t *ws, void *stream) {
+}  // extern "C"
+
+namespace {
+
+enum Phase { kRotate = 1, kLinear = 2 };
+
+// The whole call: checks, plans, workspace layout, then the rotation launch
+// (phase kRotate) and the linear launch (phase kLinear).
+int run_group(int32_t n_members, const exl3_weight_t *const *w, const void *x, int64_t ldx, int64_t M,
+              void *const *y, const int64_t *ldy, const exl3_workspace_t *ws, void *stream, int phases) {
   MemberPlan mp[kMaxMembers];
   int e = check_group(n_members, w, M, mp);
   if (e != EXL3_OK) return e;
-  if (!y || !ldy) return EXL3_EINVAL;
+  if ((phases & kLinear) && (!y || !ldy)) return EXL3_EINVAL;
   if (M == 0) return EXL3_OK;
   const int64_t K = w[0]->K;
-  if (!x || ldx < K || (uintptr_t)x % 2 != 0) return x && ldx >= K ? EXL3_EALIGN : EXL3_EINVAL;
-  for (int j = 0; j < n_members; ++j) {
-    if (!y[j] || ldy[j] < w[j]->N) return EXL3_EINVAL;
-    if ((uintptr_t)y[j] % 2 != 0) return EXL3_EALIGN;
+  if (phases & kRotate) {
+    if (!x || ldx < K) return EXL3_EINVAL;
+    if ((uintptr_t)x % 2 != 0) return EXL3_EALIGN;
+  }
+  if (phases & kLinear) {
+    for (int j = 0; j < n_members; ++j) {
+      if (!y[j] || ldy[j] < w[j]->N) return EXL3_EINVAL;
+      if ((uintptr_t)y[j] % 2 != 0) return EXL3_EALIGN;
+    }
   }
   if (!ws || !ws->ptr) return EXL3_EWORKSPACE;
 
@@ -265,8 +279,8 @@ int exl3_linear_group(int32_t n_members, const exl3_weight_t *const *w, const vo
     m.scales = (const uint16_t *)wj->scales;
     m.svh = (const uint16_t *)wj->svh;
     m.xr = xr;
-    m.y = (uint16_t *)y[j];
-    m.ldy = ldy[j];
+    m.y = (phases & kLinear) ? (uint16_t *)y[j] : nullptr;
+    m.ldy = (phases & kLinear) ? ldy[j] : 0;
     m.block_stride = wj->block_stride;
     m.N = (int32_t)wj->N;
     m.n_blocks = mp[j].n_blocks;
@@ -297,16 +311,41 @@ int exl3_linear_group(int32_t n_members, const exl3_weight_t *const *w, const vo
   la.total_wgs = (int32_t)wg;
 
   if (g_hooks.mock) {
-    g_hooks.launches += 2;
+    g_hooks.launches += ((phases & kRotate) ? 1 : 0) + ((phases & kLinear) ? 1 : 0);
     g_hooks.last_stream = stream;
     return EXL3_OK;
   }
-  e = exl3::launch_rot(ra, stream);
-  if (e) return hip_fail(e);
-  e = exl3::launch_linear(la, w[0]->bits, L.m_tiles, L.chained, stream);
-  if (e) return hip_fail(e);
+  if (phases & kRotate) {
+    e = exl3::launch_rot(ra, stream);
+    if (e) return hip_fail(e);
+  }
+  if (phases & kLinear) {
+    e = exl3::launch_linear(la, w[0]->bits, L.m_tiles, L.chained, stream);
+    if (e) return hip_fail(e);
+  }
   return EXL3_OK;
 }
+
+}  // namespace
+
+extern "C" {
+
+int exl3_linear_group(int32_t n_members, const exl3_weight_t *const *w, const void *x, int64_t ldx, int64_t M,
+                      void *const *y, const int64_t *ldy, const exl3_workspace_t *ws, void *stream) {
+  return run_group(n_members, w, x, ldx, M, y, ldy, ws, stream, kRotate | kLinear);
+}
+
+int exl3_rotate(int32_t n_members, const exl3_weight_t *const *w, const void *x, int64_t ldx, int64_t M,
+                const exl3_workspace_t *ws, void *stream) {
+  return run_group(n_members, w, x, ldx, M, nullptr, nullptr, ws, stream, kRotate);
+}
+
+int exl3_linear_rotated(int32_t n_members, const exl3_weight_t *const *w, int64_t M, void *const *y,
+                        const int64_t *ldy, const exl3_workspace_t *ws, void *stream) {
+  return run_group(n_members, w, nullptr, 0, M, y, ldy, ws, stream, kLinear);
+}
+
+
 
 int exl3_linear(const exl3_weight_t *w, const void *x, int64_t ldx, int64_t M, void *y, int64_t ldy,
                 const exl3_workspace_t *ws, void *stream) {

@@ -69,6 +69,9 @@ _SIGNATURES = {
     "exl3_linear": (ctypes.c_int, [W_P, P, I64, I64, P, I64, ctypes.POINTER(exl3_workspace_t), P]),
     "exl3_linear_group": (ctypes.c_int, [I32, ctypes.POINTER(W_P), P, I64, I64, PP, ctypes.POINTER(I64),
                                          ctypes.POINTER(exl3_workspace_t), P]),
+    "exl3_rotate": (ctypes.c_int, [I32, ctypes.POINTER(W_P), P, I64, I64, ctypes.POINTER(exl3_workspace_t), P]),
+    "exl3_linear_rotated": (ctypes.c_int, [I32, ctypes.POINTER(W_P), I64, PP, ctypes.POINTER(I64),
+                                           ctypes.POINTER(exl3_workspace_t), P]),
     "exl3_strerror": (ctypes.c_char_p, [ctypes.c_int]),
     "exl3_last_hip_error": (ctypes.c_int, []),
     "exl3_test_dequant": (ctypes.c_int, [W_P, P, P]),
@@ -226,6 +229,23 @@ def exl3_linear_group(weights: Sequence[Weight], x, ys, ws: Workspace, stream=No
     ld = (I64 * n)(*[y.stride(0) for y in ys])
     _check(lib().exl3_linear_group(n, _wlist(weights), _ptr(x), x.stride(0), M, yp, ld, ctypes.byref(ws.ws),
                                    _stream_handle(stream)), "exl3_linear_group")
+    return ys
+
+
+def exl3_rotate(weights: Sequence[Weight], x, ws: Workspace, stream=None, M: Optional[int] = None):
+    """First launch of the group call: rotate x for every member into ws."""
+    M = x.shape[0] if M is None else M
+    _check(lib().exl3_rotate(len(weights), _wlist(weights), _ptr(x), x.stride(0), M, ctypes.byref(ws.ws),
+                             _stream_handle(stream)), "exl3_rotate")
+
+
+def exl3_linear_rotated(weights: Sequence[Weight], ys, ws: Workspace, M: int, stream=None):
+    """Second launch: the linear on the rotated input held by ws."""
+    n = len(weights)
+    yp = (ctypes.c_void_p * n)(*[_ptr(y) for y in ys])
+    ld = (I64 * n)(*[y.stride(0) for y in ys])
+    _check(lib().exl3_linear_rotated(n, _wlist(weights), M, yp, ld, ctypes.byref(ws.ws), _stream_handle(stream)),
+           "exl3_linear_rotated")
     return ys
 
 
