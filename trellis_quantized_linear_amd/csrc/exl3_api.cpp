@@ -285,16 +285,15 @@ int run_group(int32_t n_members, const exl3_weight_t *const *w, const void *x, i
     m.N = (int32_t)wj->N;
     m.n_blocks = mp[j].n_blocks;
     m.splits = mp[j].splits;
+    m.groups = exl3::groups_per_block(mp[j].splits, L.m_tiles, L.chained);
     m.wg_begin = (int32_t)wg;
     if (!L.chained) {
       m.partials = (float *)(base + off);
       off += lay.part_bytes[j];
       m.counters = (uint32_t *)base + counter_off;
       counter_off += (size_t)L.row_blocks * mp[j].n_blocks;
-      wg += L.row_blocks * mp[j].n_blocks * mp[j].splits;
-    } else {
-      wg += L.row_blocks * mp[j].n_blocks;
     }
+    wg += L.row_blocks * mp[j].n_blocks * m.groups;
   }
   if (wg >= (int64_t(1) << 31)) return EXL3_EINVAL;
   ra.x = (const uint16_t *)x;

@@ -27,6 +27,7 @@ struct MemberArgs {
   int32_t N;
   int32_t n_blocks;
   int32_t splits;             // S of the plan
+  int32_t groups;             // workgroups per (row block, column block); 1 when chained
   int32_t wg_begin;           // first workgroup of this member in the grid
 };
 
@@ -58,6 +59,15 @@ struct DequantArgs {
   int32_t K;
   int32_t N;
 };
+
+// Workgroups per (row block, column block) of a launch: one when every split
+// of a block runs in one workgroup; else ceil(S / 4) for the row tilings of
+// up to 32 rows (one split per wave) and S for larger tilings (one split per
+// workgroup).
+inline int groups_per_block(int splits, int m_tiles, bool chained) {
+  if (chained) return 1;
+  return m_tiles <= 2 ? (splits + kWaves - 1) / kWaves : splits;
+}
 
 // Launchers (exl3_kernels.hip). Each returns a hipError_t as int.
 int launch_linear(const LinearArgs &a, int bits, int m_tiles, bool chained, void *stream);

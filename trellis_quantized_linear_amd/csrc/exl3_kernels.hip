@@ -36,6 +36,10 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 // rows beyond M with zeros without a branch.
 constexpr int kRsrcWord3 = 0x00020000;
 constexpr uint32_t kOutOfRange = 0x80000000u;
+// s_waitcnt operand for vmcnt(0) with expcnt and lgkmcnt left at their
+// maxima (gfx9 encoding: vmcnt[3:0] bits 3:0, expcnt 6:4, lgkmcnt 11:8,
+// vmcnt[5:4] bits 15:14).
+constexpr int kWaitVmcnt0 = 0x0F70;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, kRsrcWord3);
@@ -49,10 +53,23 @@ constexpr unsigned short kCbAdd = 31161;
 constexpr uint32_t kCbMask2 = 0x8FFF8FFFu;
 constexpr uint32_t kCbBase2 = 0x30003000u;
 
-__device__ __forceinline__ uint32_t codebook2(uint32_t states2) {
+// The and-or constants live in VGPRs: gfx9 VOP3 instructions take no
+// literal, and with the constants in registers the mask and the or fuse into
+// one v_and_or_b32 per two weights.
+struct CbConst {
+  uint32_t mask2, base2;
+};
+
+__device__ __forceinline__ CbConst cb_const() {
+  CbConst c{kCbMask2, kCbBase2};
+  asm volatile("" : "+v"(c.mask2), "+v"(c.base2));
+  return c;
+}
+
+__device__ __forceinline__ uint32_t codebook2(uint32_t states2, const CbConst &cb) {
   const u16x2 s = __builtin_bit_cast(u16x2, states2);
   const u16x2 t = s * u16x2{kCbMul, kCbMul} + u16x2{kCbAdd, kCbAdd};
-  return (__builtin_bit_cast(uint32_t, t) & kCbMask2) | kCbBase2;
+  return (__builtin_bit_cast(uint32_t, t) & cb.mask2) | cb.base2;
 }
 
 // ------------------------------------------------------------ trellis decode
@@ -135,7 +152,8 @@ __device__ __forceinline__ BLane<BITS> b_lane(int lane) {
 }
 
 template <int BITS>
-__device__ __forceinline__ half8 decode8(const uint32_t (&w)[BitsTraits<BITS>::kDwords], uint32_t shift) {
+__device__ __forceinline__ half8 decode8(const uint32_t (&w)[BitsTraits<BITS>::kDwords], uint32_t shift,
+                                        const CbConst &cb) {
   uint32_t v0, v1, v2;
   const uint32_t w2 = BitsTraits<BITS>::kDwords > 2 ? w[BitsTraits<BITS>::kDwords - 1] : 0u;
   if constexpr (BitsTraits<BITS>::kAligned) {
@@ -146,10 +164,10 @@ __device__ __forceinline__ half8 decode8(const uint32_t (&w)[BitsTraits<BITS>::k
     v2 = w2 >> shift;
   }
   u32x4 r;
-  r[0] = codebook2(window_pair<BITS, 0>(v0, v1, v2));
-  r[1] = codebook2(window_pair<BITS, 1>(v0, v1, v2));
-  r[2] = codebook2(window_pair<BITS, 2>(v0, v1, v2));
-  r[3] = codebook2(window_pair<BITS, 3>(v0, v1, v2));
+  r[0] = codebook2(window_pair<BITS, 0>(v0, v1, v2), cb);
+  r[1] = codebook2(window_pair<BITS, 1>(v0, v1, v2), cb);
+  r[2] = codebook2(window_pair<BITS, 2>(v0, v1, v2), cb);
+  r[3] = codebook2(window_pair<BITS, 3>(v0, v1, v2), cb);
   return __builtin_bit_cast(half8, r);
 }
 
@@ -233,8 +251,9 @@ __global__ __launch_bounds__(kThreads) void rot_kernel(const RotArgs a) {
 
 // ------------------------------------------------------------ linear
 
+// Chunks in flight per wave: deeper where a stage is small.
 template <int MT>
-struct Depth { static constexpr int P = MT == 1 ? 4 : (MT == 2 ? 3 : 2); };   // chunks in flight
+struct Depth { static constexpr int P = MT == 1 ? 8 : (MT == 2 ? 4 : 2); };
 
 template <int BITS, int MT>
 struct Stage {
@@ -260,10 +279,11 @@ __device__ __forceinline__ void load_stage(Stage<BITS, MT> &st, __amdgpu_buffer_
 }
 
 template <int BITS, int MT>
-__device__ __forceinline__ void compute_stage(const Stage<BITS, MT> &st, uint32_t shift, f32x4 (&acc)[MT][2]) {
+__device__ __forceinline__ void compute_stage(const Stage<BITS, MT> &st, uint32_t shift, const CbConst &cb,
+                                              f32x4 (&acc)[MT][2]) {
   half8 bf[2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) bf[i] = decode8<BITS>(st.b[i], shift);
+  for (int i = 0; i < 2; ++i) bf[i] = decode8<BITS>(st.b[i], shift, cb);
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     const half8 af = __builtin_bit_cast(half8, st.a[mt]);
@@ -273,34 +293,8 @@ __device__ __forceinline__ void compute_stage(const Stage<BITS, MT> &st, uint32_
   }
 }
 
-// One K-split chain: chunks [c0, c1) in ascending order, from zero.
-template <int BITS, int MT>
-__device__ __forceinline__ void run_chain(f32x4 (&acc)[MT][2], __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
-                                          const uint32_t (&voff_a)[MT],
-                                          const uint32_t (&voff_b)[2][BitsTraits<BITS>::kDwords],
-                                          uint32_t shift, int c0, int c1) {
-  constexpr int P = Depth<MT>::P;
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int i = 0; i < 2; ++i) acc[mt][i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  Stage<BITS, MT> st[P];
-#pragma unroll
-  for (int p = 0; p < P; ++p)
-    if (c0 + p < c1) load_stage<BITS, MT>(st[p], ra, rb, voff_a, voff_b, c0 + p);
-  for (int c = c0; c < c1; c += P) {
-#pragma unroll
-    for (int p = 0; p < P; ++p) {
-      if (c + p < c1) {
-        compute_stage<BITS, MT>(st[p], shift, acc);
-        if (c + p + P < c1) load_stage<BITS, MT>(st[p], ra, rb, voff_a, voff_b, c + p + P);
-      }
-    }
-  }
-}
-
 template <int BITS, int MT, bool CHAINED>
-__global__ __launch_bounds__(kThreads) void linear_kernel(const LinearArgs a) {
+__global__ __launch_bounds__(kThreads) void linear_ntile_kernel(const LinearArgs a) {
   using T = BitsTraits<BITS>;
   constexpr int R = 16 * MT;                      // rows per workgroup
   const int lane = threadIdx.x & 63;
@@ -313,7 +307,7 @@ __global__ __launch_bounds__(kThreads) void linear_kernel(const LinearArgs a) {
   if (a.n_members > 2 && bid >= a.m[2].wg_begin) j = 2;
   const MemberArgs &m = a.m[j];
   const int S = m.splits;
-  const int groups = CHAINED ? 1 : S;             // workgroups per (row block, column block)
+  const int groups = m.groups;                    // workgroups per (row block, column block): 1 or S
   const int local = bid - m.wg_begin;
   const int per_rb = m.n_blocks * groups;
   const int rb = local / per_rb;
@@ -344,18 +338,57 @@ __global__ __launch_bounds__(kThreads) void linear_kernel(const LinearArgs a) {
 #pragma unroll
     for (int d = 0; d < T::kDwords; ++d) voff_b[i][d] = bl.voff[d] + (uint32_t)((2 * wave + i) * T::kTileBytes);
 
+  // The workgroup's chunks [cb, ce) hold chains s_begin .. s_end-1; split s
+  // covers chunks [floor(s*C/S), floor((s+1)*C/S)). One pipelined loop runs
+  // over all of them; at each chain's last chunk the chain's sum is folded
+  // into z in split order (z = P0, then z + P1, ...) and the accumulator
+  // restarts from zero, exactly as if every chain ran in its own workgroup.
+  constexpr int P = Depth<MT>::P;
+  const CbConst cbc = cb_const();
+  const int cb = (int)(((int64_t)s_begin * C) / S);
+  const int ce = (int)(((int64_t)s_end * C) / S);
+  const int last = ce - 1;
+  int s = s_begin;
+  int bnd = (int)(((int64_t)(s + 1) * C) / S);
   f32x4 acc[MT][2];
   f32x4 z[CHAINED ? MT : 1][2];
-  for (int s = s_begin; s < s_end; ++s) {
-    const int c0 = (int)(((int64_t)s * C) / S);
-    const int c1 = (int)(((int64_t)(s + 1) * C) / S);
-    run_chain<BITS, MT>(acc, ra, rbuf, voff_a, voff_b, bl.shift, c0, c1);
-    if constexpr (CHAINED) {
-      // splits added left to right: ((P0 + P1) + P2) + ...
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
+  for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int i = 0; i < 2; ++i) z[mt][i] = (s == 0) ? acc[mt][i] : z[mt][i] + acc[mt][i];
+    for (int i = 0; i < 2; ++i) acc[mt][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // Stage loads are issued strictly in stage order (the scheduling barriers
+  // keep the prologue's loads from being regrouped), so the outstanding-load
+  // count when a stage is consumed is the same on entry and on the back edge.
+  Stage<BITS, MT> st[P];
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+    load_stage<BITS, MT>(st[p], ra, rbuf, voff_a, voff_b, min(cb + p, last));
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  for (int c = cb; c < ce; c += P) {
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      const int cc = c + p;
+      if (cc < ce) {
+        compute_stage<BITS, MT>(st[p], bl.shift, cbc, acc);
+        if constexpr (CHAINED) {
+          if (cc + 1 == bnd) {                    // chain s complete (uniform branch)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+              for (int i = 0; i < 2; ++i) {
+                z[mt][i] = (s == 0) ? acc[mt][i] : z[mt][i] + acc[mt][i];
+                acc[mt][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+              }
+            ++s;
+            bnd = (int)(((int64_t)(s + 1) * C) / S);
+          }
+        }
+      }
+      // unconditional (clamped) prefetch keeps the outstanding-load count
+      // static, so each stage waits only for its own loads
+      load_stage<BITS, MT>(st[p], ra, rbuf, voff_a, voff_b, min(cc + P, last));
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 
@@ -384,7 +417,12 @@ __global__ __launch_bounds__(kThreads) void linear_kernel(const LinearArgs a) {
       }
     }
   } else {
-    // write this split's fp32 partial P_s[row][col]
+    // Write this split's fp32 partial P_s[row][col] with agent-scope stores
+    // (written through the XCD's non-coherent L2), wait until every wave's
+    // stores have completed, then count the arrival. The last arriver reads
+    // all partials with agent-scope loads (fetched past stale cache lines),
+    // adds them in split order and resets the counter: no L2 write-back or
+    // invalidation is needed on either side.
     const int N = m.N;
     float *P = m.partials + (int64_t)s_begin * M * N + col0;
 #pragma unroll
@@ -394,20 +432,20 @@ __global__ __launch_bounds__(kThreads) void linear_kernel(const LinearArgs a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int row = row_base + 16 * mt + 4 * g + r;
-          if (row < M) P[(int64_t)row * N + 16 * (2 * wave + i) + c] = acc[mt][i][r];
+          if (row < M)
+            __hip_atomic_store(P + (int64_t)row * N + 16 * (2 * wave + i) + c, acc[mt][i][r], __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
         }
-    // publish: every wave's stores reach memory before the counter moves
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);        // this wave's stores are complete
     __syncthreads();
     __shared__ int s_last;
     uint32_t *counter = m.counters + (int64_t)rb * m.n_blocks + nb;
     if (threadIdx.x == 0) {
       const uint32_t prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      s_last = prev == (uint32_t)(S - 1);
+      s_last = prev == (uint32_t)(groups - 1);
     }
     __syncthreads();
     if (!s_last) return;
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     // the last arriver resets the counter it consumed: zero at rest
     if (threadIdx.x == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const float *P0 = m.partials + col0;
@@ -416,14 +454,264 @@ __global__ __launch_bounds__(kThreads) void linear_kernel(const LinearArgs a) {
       const int row = row_base + rr;
       if (row >= M) break;
       const float *p = P0 + (int64_t)row * N;
-      float z0 = p[lane], z1 = p[lane + 64];
-      for (int s = 1; s < S; ++s) {
+      float z0 = __hip_atomic_load(p + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      float z1 = __hip_atomic_load(p + lane + 64, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (int sp = 1; sp < S; ++sp) {
         p += split_stride;
-        z0 = z0 + p[lane];
-        z1 = z1 + p[lane + 64];
+        z0 = z0 + __hip_atomic_load(p + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        z1 = z1 + __hip_atomic_load(p + lane + 64, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
       epilogue_row(z0, z1, lane, sc0, sc1, sv0, sv1, m.y + (int64_t)row * m.ldy + col0);
     }
+  }
+}
+
+
+// ------------------------------------------------------------ linear, one split per wave
+//
+// Row tilings of 16 and 32 rows. Wave w of a workgroup runs whole K-split
+// chains over all 8 column tiles of the block, so one A fragment (the rotated
+// input, 16 rows x 32 K) feeds 8 MFMAs instead of 2. Chains are assigned
+// round-robin: when the workgroup owns every split of its block (chained),
+// wave w runs splits w, w+4, ...; otherwise workgroup g owns splits 4g..4g+3,
+// one per wave. A lane reads its 2 or 3 dwords of a tile row pair with one
+// load; the two lanes whose windows wrap past the end of their tile (j = 31)
+// take their last dword from the lane that holds the tile's first dword.
+
+template <int MT>
+struct ChainDepth { static constexpr int P = MT == 1 ? 4 : 3; };
+
+template <int BITS, int MT>
+struct ChainStage {
+  u32x4 a[MT];
+  uint32_t b[8][BitsTraits<BITS>::kDwords];
+};
+
+template <int BITS>
+__device__ __forceinline__ void load_b_words(uint32_t (&w)[BitsTraits<BITS>::kDwords], __amdgpu_buffer_rsrc_t rb,
+                                             uint32_t voff, int soff) {
+  if constexpr (BitsTraits<BITS>::kDwords == 2) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b64(rb, (int)voff, soff, 0);
+    w[0] = v[0];
+    w[1] = v[1];
+  } else {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b96(rb, (int)voff, soff, 0);
+    w[0] = v[0];
+    w[1] = v[1];
+    w[2] = v[2];
+  }
+}
+
+template <int BITS, int MT>
+__device__ __forceinline__ void load_chain_stage(ChainStage<BITS, MT> &st, __amdgpu_buffer_rsrc_t ra,
+                                                 __amdgpu_buffer_rsrc_t rb, const uint32_t (&voff_a)[MT],
+                                                 uint32_t voff_b, int chunk) {
+  const int soff_a = chunk * 64;
+  const int soff_b = chunk * 512 * BITS;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+    st.a[mt] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, (int)voff_a[mt], soff_a, 0));
+#pragma unroll
+  for (int t = 0; t < 8; ++t)
+    load_b_words<BITS>(st.b[t], rb, voff_b + (uint32_t)(t * BitsTraits<BITS>::kTileBytes), soff_b);
+}
+
+template <int BITS, int MT>
+__device__ __forceinline__ void compute_chain_stage(ChainStage<BITS, MT> &st, uint32_t shift, bool wrap_lane,
+                                                    int lane, const CbConst &cb, f32x4 (&acc)[MT][8]) {
+  constexpr int ND = BitsTraits<BITS>::kDwords;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    // tail-biting: the last dword of lanes 31 and 63 is their tile's dword 0
+    const uint32_t first = __shfl(st.b[t][0], lane & 32, 64);
+    if (wrap_lane) st.b[t][ND - 1] = first;
+    const half8 bf = decode8<BITS>(st.b[t], shift, cb);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+      acc[mt][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, st.a[mt]), bf, acc[mt][t], 0, 0, 0);
+  }
+}
+
+template <int BITS, int MT, bool CHAINED>
+__global__ __launch_bounds__(kThreads) void linear_chain_kernel(const LinearArgs a) {
+  constexpr int R = 16 * MT;
+  constexpr int P = ChainDepth<MT>::P;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int bid = blockIdx.x;
+  int j = 0;
+  if (a.n_members > 1 && bid >= a.m[1].wg_begin) j = 1;
+  if (a.n_members > 2 && bid >= a.m[2].wg_begin) j = 2;
+  const MemberArgs &m = a.m[j];
+  const int S = m.splits;
+  const int groups = m.groups;
+  const int local = bid - m.wg_begin;
+  const int per_rb = m.n_blocks * groups;
+  const int rb = local / per_rb;
+  const int rem = local - rb * per_rb;
+  const int nb = rem / groups;
+  const int sg = rem - nb * groups;
+  const int M = a.M, K = a.K, C = a.chunks;
+  const int row_base = rb * R;
+  const int col0 = nb * kBlockCols;
+
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(m.xr, (uint32_t)((uint64_t)M * K * 2));
+  const __amdgpu_buffer_rsrc_t rbuf = make_rsrc(m.words + (int64_t)nb * m.block_stride, (uint32_t)(16u * K * BITS));
+  const int c = lane & 15, g = lane >> 4;
+  uint32_t voff_a[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int row = row_base + 16 * mt + c;
+    voff_a[mt] = row < M ? (uint32_t)(row * 2 * K + 16 * g) : kOutOfRange;
+  }
+  const int jseg = 2 * c + (g & 1);
+  const uint32_t shift = 8u * (uint32_t)((BITS * jseg) & 3);
+  const uint32_t voff_b = (uint32_t)((g >> 1) * 8 * BitsTraits<BITS>::kTileBytes + 4 * ((BITS * jseg) >> 2));
+  const bool wrap_lane = jseg == 31;
+  const CbConst cbc = cb_const();
+
+  // splits of this wave: CHAINED: w, w+4, ...; else 4*sg + w (if it exists)
+  const int s_first = CHAINED ? wave : kWaves * sg + wave;
+  const int s_step = CHAINED ? kWaves : S;              // one split per wave when not chained
+  const int rounds = CHAINED ? (S + kWaves - 1) / kWaves : 1;
+
+  f32x4 z[CHAINED ? MT : 1][8];                         // running split-order sum (chained)
+  __shared__ float pbuf[CHAINED ? kWaves : 1][CHAINED ? R : 1][kBlockCols];
+  float zsum[CHAINED ? R * kBlockCols / kThreads : 1];
+
+  for (int round = 0; round < rounds; ++round) {
+    const int s = s_first + round * (CHAINED ? kWaves : 0);
+    const bool active = s < S;                           // uniform per wave
+    f32x4 acc[MT][8];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int t = 0; t < 8; ++t) acc[mt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (active) {
+      const int c0 = (int)(((int64_t)s * C) / S);
+      const int c1 = (int)(((int64_t)(s + 1) * C) / S);
+      const int last = c1 - 1;
+      ChainStage<BITS, MT> st[P];
+#pragma unroll
+      for (int p = 0; p < P; ++p) {
+        load_chain_stage<BITS, MT>(st[p], ra, rbuf, voff_a, voff_b, min(c0 + p, last));
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      for (int cc0 = c0; cc0 < c1; cc0 += P) {
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+          const int cc = cc0 + p;
+          if (cc < c1) compute_chain_stage<BITS, MT>(st[p], shift, wrap_lane, lane, cbc, acc);
+          load_chain_stage<BITS, MT>(st[p], ra, rbuf, voff_a, voff_b, min(cc + P, last));
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    }
+    (void)s_step;
+    if constexpr (CHAINED) {
+      // fold this round's chains into the running sum in split order
+      __syncthreads();
+      if (active) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int t = 0; t < 8; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) pbuf[wave][16 * mt + 4 * g + r][16 * t + c] = acc[mt][t][r];
+      }
+      __syncthreads();
+      const int in_round = min(kWaves, S - round * kWaves);
+#pragma unroll
+      for (int e = 0; e < R * kBlockCols / kThreads; ++e) {
+        const int idx = threadIdx.x + e * kThreads;
+        const int row = idx / kBlockCols, col = idx % kBlockCols;
+        float v = round == 0 ? pbuf[0][row][col] : zsum[e] + pbuf[0][row][col];
+        for (int w = 1; w < in_round; ++w) v = v + pbuf[w][row][col];
+        zsum[e] = v;
+      }
+    } else {
+      // write this wave's split partial P_s with agent-scope stores
+      if (active) {
+        const int N = m.N;
+        float *P = m.partials + (int64_t)s * M * N + col0;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int t = 0; t < 8; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int row = row_base + 16 * mt + 4 * g + r;
+              if (row < M)
+                __hip_atomic_store(P + (int64_t)row * N + 16 * t + c, acc[mt][t][r], __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+            }
+      }
+    }
+  }
+  (void)z;
+
+  const float sc0 = fp16_to_f32(m.scales[col0 + lane]);
+  const float sc1 = fp16_to_f32(m.scales[col0 + lane + 64]);
+  const float sv0 = fp16_to_f32(m.svh[col0 + lane]);
+  const float sv1 = fp16_to_f32(m.svh[col0 + lane + 64]);
+  __shared__ float zrow[R][kBlockCols];
+
+  if constexpr (CHAINED) {
+#pragma unroll
+    for (int e = 0; e < R * kBlockCols / kThreads; ++e) {
+      const int idx = threadIdx.x + e * kThreads;
+      zrow[idx / kBlockCols][idx % kBlockCols] = zsum[e];
+    }
+  } else {
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);             // this wave's partial stores are complete
+    __syncthreads();
+    __shared__ int s_last;
+    uint32_t *counter = m.counters + (int64_t)rb * m.n_blocks + nb;
+    if (threadIdx.x == 0) {
+      const uint32_t prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_last = prev == (uint32_t)(groups - 1);
+    }
+    __syncthreads();
+    if (!s_last) return;
+    if (threadIdx.x == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // Sum the S partials in split order: every thread owns float4 columns of
+    // the block's rows; loads are issued 8 splits at a time (clamped to the
+    // last split, so the load count is static) before they are added.
+    const int N = m.N;
+    const int64_t split_stride = (int64_t)M * N;
+#pragma unroll
+    for (int e = 0; e < R * kBlockCols / 4 / kThreads; ++e) {
+      const int idx = threadIdx.x + e * kThreads;        // float4 index in the block
+      const int rr = idx / (kBlockCols / 4), c4 = idx % (kBlockCols / 4);
+      const int row = row_base + rr;
+      f32x4 zv = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (row < M) {
+        const f32x4 *p = (const f32x4 *)(m.partials + (int64_t)row * N + col0) + c4;
+        for (int s0 = 0; s0 < S; s0 += 8) {
+          f32x4 v[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const int sp = min(s0 + u, S - 1);
+            const float *q = (const float *)(p + (sp * split_stride) / 4);
+            v[u] = f32x4{__hip_atomic_load(q + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+                         __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+                         __hip_atomic_load(q + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+                         __hip_atomic_load(q + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)};
+          }
+#pragma unroll
+          for (int u = 0; u < 8; ++u)
+            if (s0 + u < S) zv = (s0 + u == 0) ? v[u] : zv + v[u];
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) zrow[rr][4 * c4 + q] = zv[q];
+    }
+  }
+  __syncthreads();
+  for (int rr = wave; rr < R; rr += kWaves) {
+    const int row = row_base + rr;
+    if (row >= M) break;
+    epilogue_row(zrow[rr][lane], zrow[rr][lane + 64], lane, sc0, sc1, sv0, sv1, m.y + (int64_t)row * m.ldy + col0);
   }
 }
 
@@ -446,7 +734,7 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const DequantArgs a) 
     for (int d = 0; d < T::kDwords; ++d)
       w[d] = __builtin_amdgcn_raw_buffer_load_b32(rbuf, (int)(bl.voff[d] + (2 * wave + i) * T::kTileBytes),
                                                   chunk * 512 * BITS, 0);
-    const u32x4 v = __builtin_bit_cast(u32x4, decode8<BITS>(w, bl.shift));
+    const u32x4 v = __builtin_bit_cast(u32x4, decode8<BITS>(w, bl.shift, cb_const()));
     const int kbase = 16 * (2 * chunk + (g >> 1)) + 8 * (g & 1);
     const int n = nb * kBlockCols + 16 * (2 * wave + i) + c;
 #pragma unroll
@@ -463,7 +751,7 @@ __global__ void codebook_kernel(const uint16_t *states, uint16_t *out, int64_t n
   if (i0 >= n) return;
   const uint32_t s0 = states[i0];
   const uint32_t s1 = (i0 + 1 < n) ? states[i0 + 1] : 0u;
-  const uint32_t w = codebook2(s0 | (s1 << 16));
+  const uint32_t w = codebook2(s0 | (s1 << 16), cb_const());
   out[i0] = (uint16_t)(w & 0xFFFFu);
   if (i0 + 1 < n) out[i0 + 1] = (uint16_t)(w >> 16);
 }
@@ -479,10 +767,10 @@ typedef void (*LinearFn)(const LinearArgs);
 
 template <int BITS, bool CHAINED>
 constexpr LinearFn pick_mt(int mti) {
-  return mti == 0 ? linear_kernel<BITS, 1, CHAINED>
-       : mti == 1 ? linear_kernel<BITS, 2, CHAINED>
-       : mti == 2 ? linear_kernel<BITS, 4, CHAINED>
-                  : linear_kernel<BITS, 8, CHAINED>;
+  return mti == 0 ? linear_chain_kernel<BITS, 1, CHAINED>
+       : mti == 1 ? linear_chain_kernel<BITS, 2, CHAINED>
+       : mti == 2 ? linear_ntile_kernel<BITS, 4, CHAINED>
+                  : linear_ntile_kernel<BITS, 8, CHAINED>;
 }
 
 template <int BITS>
@@ -505,6 +793,7 @@ int launch_linear(const LinearArgs &a, int bits, int m_tiles, bool chained, void
     case 8: fn = pick_linear<8>(mti, chained); break;
     default: return (int)hipErrorInvalidValue;
   }
+  (void)hipGetLastError();   // report this launch's error, not an earlier one
   hipLaunchKernelGGL(fn, dim3((unsigned)a.total_wgs), dim3(kThreads), 0, (hipStream_t)stream, a);
   return (int)hipGetLastError();
 }
@@ -512,6 +801,7 @@ int launch_linear(const LinearArgs &a, int bits, int m_tiles, bool chained, void
 int launch_rot(const RotArgs &a, void *stream) {
   const int64_t items = (int64_t)a.n_members * a.M * (a.K / 128);
   const int64_t wgs = (items + kWaves - 1) / kWaves;
+  (void)hipGetLastError();
   hipLaunchKernelGGL(rot_kernel, dim3((unsigned)wgs), dim3(kThreads), 0, (hipStream_t)stream, a);
   return (int)hipGetLastError();
 }
@@ -520,6 +810,7 @@ int launch_dequant(const DequantArgs &a, int bits, void *stream) {
   const unsigned wgs = (unsigned)((a.N / kBlockCols) * (a.K / kChunk));
   const dim3 grid(wgs), block(kThreads);
   hipStream_t s = (hipStream_t)stream;
+  (void)hipGetLastError();
   switch (bits) {
     case 2: hipLaunchKernelGGL(dequant_kernel<2>, grid, block, 0, s, a); break;
     case 3: hipLaunchKernelGGL(dequant_kernel<3>, grid, block, 0, s, a); break;
@@ -536,6 +827,7 @@ int launch_dequant(const DequantArgs &a, int bits, void *stream) {
 int launch_codebook(const uint16_t *states, uint16_t *out, int64_t n, void *stream) {
   const int64_t pairs = (n + 1) / 2;
   const unsigned wgs = (unsigned)((pairs + 255) / 256);
+  (void)hipGetLastError();
   hipLaunchKernelGGL(codebook_kernel, dim3(wgs), dim3(256), 0, (hipStream_t)stream, states, out, n);
   return (int)hipGetLastError();
 }
@@ -545,6 +837,7 @@ int launch_fill_zero(void *ptr, size_t bytes, void *stream) {
   if (n == 0) return 0;
   int64_t wgs = (n + 255) / 256;
   if (wgs > 4096) wgs = 4096;
+  (void)hipGetLastError();
   hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)wgs), dim3(256), 0, (hipStream_t)stream, (uint32_t *)ptr, n);
   return (int)hipGetLastError();
 }

@@ -84,9 +84,16 @@ _SIGNATURES = {
 
 
 def lib():
-    """Load libexl3.so (built in-tree by __graft_entry__.build()); raise if absent."""
+    """Load libexl3.so (built in-tree by __graft_entry__.build()); raise if absent.
+
+    torch is imported first: it ships its own HIP runtime whose soname
+    (libamdhip64.so.7) then satisfies libexl3.so's dependency, so the process
+    holds one HIP runtime and torch's streams and pointers are valid in the
+    library. Loaded the other way round, two runtimes would coexist.
+    """
     global _LIB
     if _LIB is None:
+        import torch  # noqa: F401  (loads the HIP runtime torch was built with)
         if not os.path.exists(LIB_PATH):
             raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() first")
         handle = ctypes.CDLL(LIB_PATH)
