@@ -298,7 +298,9 @@ __global__ __launch_bounds__(kThreads) void linear_ntile_kernel(const LinearArgs
   using T = BitsTraits<BITS>;
   constexpr int R = 16 * MT;                      // rows per workgroup
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  // wave index as a scalar: everything derived from it (split, chunk,
+  // buffer offsets) stays in SGPRs
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int bid = blockIdx.x;
 
   // member of this workgroup (uniform)
@@ -338,57 +340,49 @@ __global__ __launch_bounds__(kThreads) void linear_ntile_kernel(const LinearArgs
 #pragma unroll
     for (int d = 0; d < T::kDwords; ++d) voff_b[i][d] = bl.voff[d] + (uint32_t)((2 * wave + i) * T::kTileBytes);
 
-  // The workgroup's chunks [cb, ce) hold chains s_begin .. s_end-1; split s
-  // covers chunks [floor(s*C/S), floor((s+1)*C/S)). One pipelined loop runs
-  // over all of them; at each chain's last chunk the chain's sum is folded
-  // into z in split order (z = P0, then z + P1, ...) and the accumulator
-  // restarts from zero, exactly as if every chain ran in its own workgroup.
+  // Chains s_begin .. s_end-1, one after another; split s covers chunks
+  // [floor(s*C/S), floor((s+1)*C/S)). Each chain starts from zero and is
+  // folded into z in split order (z = P0, then z + P1, ...), exactly as if
+  // every chain ran in its own workgroup.
   constexpr int P = Depth<MT>::P;
   const CbConst cbc = cb_const();
-  const int cb = (int)(((int64_t)s_begin * C) / S);
-  const int ce = (int)(((int64_t)s_end * C) / S);
-  const int last = ce - 1;
-  int s = s_begin;
-  int bnd = (int)(((int64_t)(s + 1) * C) / S);
   f32x4 acc[MT][2];
   f32x4 z[CHAINED ? MT : 1][2];
+  for (int s = s_begin; s < s_end; ++s) {
+    const int c0 = (int)(((int64_t)s * C) / S);
+    const int c1 = (int)(((int64_t)(s + 1) * C) / S);
+    const int last = c1 - 1;
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int i = 0; i < 2; ++i) acc[mt][i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // Stage loads are issued strictly in stage order (the scheduling barriers
-  // keep the prologue's loads from being regrouped), so the outstanding-load
-  // count when a stage is consumed is the same on entry and on the back edge.
-  Stage<BITS, MT> st[P];
-#pragma unroll
-  for (int p = 0; p < P; ++p) {
-    load_stage<BITS, MT>(st[p], ra, rbuf, voff_a, voff_b, min(cb + p, last));
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  for (int c = cb; c < ce; c += P) {
+      for (int i = 0; i < 2; ++i) acc[mt][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // stage loads are issued strictly in stage order (the scheduling
+    // barriers keep them from being regrouped), so the outstanding-load count
+    // when a stage is consumed is the same on entry and on the back edge
+    Stage<BITS, MT> st[P];
 #pragma unroll
     for (int p = 0; p < P; ++p) {
-      const int cc = c + p;
-      if (cc < ce) {
-        compute_stage<BITS, MT>(st[p], bl.shift, cbc, acc);
-        if constexpr (CHAINED) {
-          if (cc + 1 == bnd) {                    // chain s complete (uniform branch)
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-              for (int i = 0; i < 2; ++i) {
-                z[mt][i] = (s == 0) ? acc[mt][i] : z[mt][i] + acc[mt][i];
-                acc[mt][i] = f32x4{0.f, 0.f, 0.f, 0.f};
-              }
-            ++s;
-            bnd = (int)(((int64_t)(s + 1) * C) / S);
-          }
-        }
-      }
-      // unconditional (clamped) prefetch keeps the outstanding-load count
-      // static, so each stage waits only for its own loads
-      load_stage<BITS, MT>(st[p], ra, rbuf, voff_a, voff_b, min(cc + P, last));
+      load_stage<BITS, MT>(st[p], ra, rbuf, voff_a, voff_b, min(c0 + p, last));
       __builtin_amdgcn_sched_barrier(0);
+    }
+    const int n = c1 - c0;
+    const int full_end = c0 + (n - n % P);
+    for (int cc0 = c0; cc0 < full_end; cc0 += P) {
+#pragma unroll
+      for (int p = 0; p < P; ++p) {
+        compute_stage<BITS, MT>(st[p], bl.shift, cbc, acc);
+        load_stage<BITS, MT>(st[p], ra, rbuf, voff_a, voff_b, min(cc0 + p + P, last));
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+#pragma unroll
+    for (int p = 0; p < P - 1; ++p)
+      if (p < n % P) compute_stage<BITS, MT>(st[p], bl.shift, cbc, acc);
+    if constexpr (CHAINED) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 2; ++i) z[mt][i] = (s == 0) ? acc[mt][i] : z[mt][i] + acc[mt][i];
     }
   }
 
@@ -471,61 +465,76 @@ __global__ __launch_bounds__(kThreads) void linear_ntile_kernel(const LinearArgs
 //
 // Row tilings of 16 and 32 rows. Wave w of a workgroup runs whole K-split
 // chains over all 8 column tiles of the block, so one A fragment (the rotated
-// input, 16 rows x 32 K) feeds 8 MFMAs instead of 2. Chains are assigned
-// round-robin: when the workgroup owns every split of its block (chained),
-// wave w runs splits w, w+4, ...; otherwise workgroup g owns splits 4g..4g+3,
-// one per wave. A lane reads its 2 or 3 dwords of a tile row pair with one
-// load; the two lanes whose windows wrap past the end of their tile (j = 31)
-// take their last dword from the lane that holds the tile's first dword.
+// input, 16 rows x 32 K) feeds 8 MFMAs. Chains are assigned round-robin: when
+// the workgroup owns every split of its block (chained), wave w runs splits w,
+// w+4, ...; otherwise workgroup g owns splits 4g..4g+3, one per wave.
+//
+// Weight stream. A chunk of a block is two tile rows of 8 tiles, 512*b
+// contiguous bytes. Each wave fetches its chunks with 128-bit loads (b/2
+// instructions per chunk instead of one or two per tile and lane: the address
+// unit spends about the same time on a 64-lane load whatever its width), and
+// stages them in its own LDS region: tile tau at tau * (32b + 16), followed by
+// a copy of the tile's first dword, so the windows that wrap past the tile's
+// end (tail-biting) read on contiguously. Each lane then reads its 2 or 3
+// dwords per tile with ds_read2_b32 (+ ds_read_b32). LDS is double-buffered
+// one chunk ahead of the decode; a wave's region is its own, so no barrier is
+// needed.
+
+template <int BITS>
+struct Stream {
+  static constexpr int kChunkBytes = 512 * BITS;                 // 16 tiles
+  static constexpr int kLoads = (kChunkBytes + 1023) / 1024;     // 128-bit loads per chunk
+  static constexpr int kStride = 32 * BITS + 16;                 // padded tile in LDS
+  static constexpr int kSlot = 16 * kStride + 16;                // 16 tiles + a dump for idle lanes
+  static constexpr int kWave = 2 * kSlot;                        // double buffer
+};
 
 template <int MT>
-struct ChainDepth { static constexpr int P = MT == 1 ? 4 : 3; };
+struct ChainDepth { static constexpr int P = 4; };
 
 template <int BITS, int MT>
 struct ChainStage {
   u32x4 a[MT];
-  uint32_t b[8][BitsTraits<BITS>::kDwords];
+  u32x4 b[Stream<BITS>::kLoads];
 };
-
-template <int BITS>
-__device__ __forceinline__ void load_b_words(uint32_t (&w)[BitsTraits<BITS>::kDwords], __amdgpu_buffer_rsrc_t rb,
-                                             uint32_t voff, int soff) {
-  if constexpr (BitsTraits<BITS>::kDwords == 2) {
-    const auto v = __builtin_amdgcn_raw_buffer_load_b64(rb, (int)voff, soff, 0);
-    w[0] = v[0];
-    w[1] = v[1];
-  } else {
-    const auto v = __builtin_amdgcn_raw_buffer_load_b96(rb, (int)voff, soff, 0);
-    w[0] = v[0];
-    w[1] = v[1];
-    w[2] = v[2];
-  }
-}
 
 template <int BITS, int MT>
 __device__ __forceinline__ void load_chain_stage(ChainStage<BITS, MT> &st, __amdgpu_buffer_rsrc_t ra,
                                                  __amdgpu_buffer_rsrc_t rb, const uint32_t (&voff_a)[MT],
-                                                 uint32_t voff_b, int chunk) {
+                                                 const uint32_t (&voff_b)[Stream<BITS>::kLoads], int chunk) {
   const int soff_a = chunk * 64;
-  const int soff_b = chunk * 512 * BITS;
+  const int soff_b = chunk * Stream<BITS>::kChunkBytes;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
     st.a[mt] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, (int)voff_a[mt], soff_a, 0));
 #pragma unroll
-  for (int t = 0; t < 8; ++t)
-    load_b_words<BITS>(st.b[t], rb, voff_b + (uint32_t)(t * BitsTraits<BITS>::kTileBytes), soff_b);
+  for (int l = 0; l < Stream<BITS>::kLoads; ++l)
+    st.b[l] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, (int)voff_b[l], soff_b, 0));
+}
+
+// Copy a stage's weight bytes into LDS slot `slot` (byte address).
+template <int BITS, int MT>
+__device__ __forceinline__ void stage_to_lds(const ChainStage<BITS, MT> &st, char *slot,
+                                             const uint32_t (&wr_off)[Stream<BITS>::kLoads],
+                                             const uint32_t (&wrap_off)[Stream<BITS>::kLoads]) {
+#pragma unroll
+  for (int l = 0; l < Stream<BITS>::kLoads; ++l) {
+    *(u32x4 *)(slot + wr_off[l]) = st.b[l];
+    *(uint32_t *)(slot + wrap_off[l]) = st.b[l][0];
+  }
 }
 
 template <int BITS, int MT>
-__device__ __forceinline__ void compute_chain_stage(ChainStage<BITS, MT> &st, uint32_t shift, bool wrap_lane,
-                                                    int lane, const CbConst &cb, f32x4 (&acc)[MT][8]) {
+__device__ __forceinline__ void compute_chain_chunk(const char *slot, uint32_t rd_off, const ChainStage<BITS, MT> &st,
+                                                    uint32_t shift, const CbConst &cb, f32x4 (&acc)[MT][8]) {
   constexpr int ND = BitsTraits<BITS>::kDwords;
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
-    // tail-biting: the last dword of lanes 31 and 63 is their tile's dword 0
-    const uint32_t first = __shfl(st.b[t][0], lane & 32, 64);
-    if (wrap_lane) st.b[t][ND - 1] = first;
-    const half8 bf = decode8<BITS>(st.b[t], shift, cb);
+    const uint32_t *q = (const uint32_t *)(slot + rd_off + t * Stream<BITS>::kStride);
+    uint32_t w[ND];
+#pragma unroll
+    for (int d = 0; d < ND; ++d) w[d] = q[d];
+    const half8 bf = decode8<BITS>(w, shift, cb);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
       acc[mt][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, st.a[mt]), bf, acc[mt][t], 0, 0, 0);
@@ -534,10 +543,14 @@ __device__ __forceinline__ void compute_chain_stage(ChainStage<BITS, MT> &st, ui
 
 template <int BITS, int MT, bool CHAINED>
 __global__ __launch_bounds__(kThreads) void linear_chain_kernel(const LinearArgs a) {
+  using SB = Stream<BITS>;
   constexpr int R = 16 * MT;
   constexpr int P = ChainDepth<MT>::P;
+  static_assert(P == 4, "the chunk loop unrolls by 4 = lcm(stages, LDS slots)");
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  // wave index as a scalar: everything derived from it (split, chunk,
+  // buffer offsets) stays in SGPRs
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int bid = blockIdx.x;
   int j = 0;
   if (a.n_members > 1 && bid >= a.m[1].wg_begin) j = 1;
@@ -555,6 +568,15 @@ __global__ __launch_bounds__(kThreads) void linear_chain_kernel(const LinearArgs
   const int row_base = rb * R;
   const int col0 = nb * kBlockCols;
 
+  // LDS: per-wave weight staging during the chunk loops; afterwards the
+  // same bytes hold the chain fold buffers and the epilogue rows.
+  constexpr int kStageBytes = kWaves * SB::kWave;
+  constexpr int kFoldBytes = (CHAINED ? kWaves : 0) * R * kBlockCols * 4;
+  constexpr int kRowBytes = R * kBlockCols * 4;
+  constexpr int kLds = kStageBytes > kFoldBytes + kRowBytes ? kStageBytes : kFoldBytes + kRowBytes;
+  __shared__ __attribute__((aligned(16))) char lds[kLds];
+  char *wlds = lds + wave * SB::kWave;
+
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(m.xr, (uint32_t)((uint64_t)M * K * 2));
   const __amdgpu_buffer_rsrc_t rbuf = make_rsrc(m.words + (int64_t)nb * m.block_stride, (uint32_t)(16u * K * BITS));
   const int c = lane & 15, g = lane >> 4;
@@ -564,19 +586,26 @@ __global__ __launch_bounds__(kThreads) void linear_chain_kernel(const LinearArgs
     const int row = row_base + 16 * mt + c;
     voff_a[mt] = row < M ? (uint32_t)(row * 2 * K + 16 * g) : kOutOfRange;
   }
+  // 128-bit load l covers chunk bytes [1024 l, 1024 l + 1024); lane bytes
+  // 16 lane .. +15 of it belong to one tile (tiles are 32b bytes, a multiple
+  // of 16). Lanes past the chunk's end load its first bytes and dump them.
+  uint32_t voff_b[SB::kLoads], wr_off[SB::kLoads], wrap_off[SB::kLoads];
+#pragma unroll
+  for (int l = 0; l < SB::kLoads; ++l) {
+    const int off = 1024 * l + 16 * lane;
+    const bool valid = off < SB::kChunkBytes;
+    const int tau = off / (32 * BITS), w = off % (32 * BITS);
+    voff_b[l] = valid ? (uint32_t)off : 0u;
+    wr_off[l] = valid ? (uint32_t)(tau * SB::kStride + w) : (uint32_t)(16 * SB::kStride);
+    wrap_off[l] = valid ? (uint32_t)(tau * SB::kStride + 32 * BITS + (w == 0 ? 0 : 4)) : (uint32_t)(16 * SB::kStride);
+  }
   const int jseg = 2 * c + (g & 1);
   const uint32_t shift = 8u * (uint32_t)((BITS * jseg) & 3);
-  const uint32_t voff_b = (uint32_t)((g >> 1) * 8 * BitsTraits<BITS>::kTileBytes + 4 * ((BITS * jseg) >> 2));
-  const bool wrap_lane = jseg == 31;
+  const uint32_t rd_off = (uint32_t)((g >> 1) * 8 * SB::kStride + 4 * ((BITS * jseg) >> 2));
   const CbConst cbc = cb_const();
 
-  // splits of this wave: CHAINED: w, w+4, ...; else 4*sg + w (if it exists)
   const int s_first = CHAINED ? wave : kWaves * sg + wave;
-  const int s_step = CHAINED ? kWaves : S;              // one split per wave when not chained
   const int rounds = CHAINED ? (S + kWaves - 1) / kWaves : 1;
-
-  f32x4 z[CHAINED ? MT : 1][8];                         // running split-order sum (chained)
-  __shared__ float pbuf[CHAINED ? kWaves : 1][CHAINED ? R : 1][kBlockCols];
   float zsum[CHAINED ? R * kBlockCols / kThreads : 1];
 
   for (int round = 0; round < rounds; ++round) {
@@ -587,9 +616,11 @@ __global__ __launch_bounds__(kThreads) void linear_chain_kernel(const LinearArgs
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int t = 0; t < 8; ++t) acc[mt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (CHAINED && round > 0) __syncthreads();           // fold buffers of the last round are read
     if (active) {
       const int c0 = (int)(((int64_t)s * C) / S);
       const int c1 = (int)(((int64_t)(s + 1) * C) / S);
+      const int n = c1 - c0;
       const int last = c1 - 1;
       ChainStage<BITS, MT> st[P];
 #pragma unroll
@@ -597,71 +628,80 @@ __global__ __launch_bounds__(kThreads) void linear_chain_kernel(const LinearArgs
         load_chain_stage<BITS, MT>(st[p], ra, rbuf, voff_a, voff_b, min(c0 + p, last));
         __builtin_amdgcn_sched_barrier(0);
       }
-      for (int cc0 = c0; cc0 < c1; cc0 += P) {
+      stage_to_lds<BITS, MT>(st[0], wlds, wr_off, wrap_off);
+      // chunk i (0-based in the chain) uses VGPR stage i % 4 and LDS slot i % 2;
+      // the next chunk is copied to LDS before chunk i is decoded.
+      int i = 0;
+      for (; i + P < n; i += P) {
 #pragma unroll
         for (int p = 0; p < P; ++p) {
-          const int cc = cc0 + p;
-          if (cc < c1) compute_chain_stage<BITS, MT>(st[p], shift, wrap_lane, lane, cbc, acc);
-          load_chain_stage<BITS, MT>(st[p], ra, rbuf, voff_a, voff_b, min(cc + P, last));
+          stage_to_lds<BITS, MT>(st[(p + 1) % P], wlds + ((p + 1) % 2) * SB::kSlot, wr_off, wrap_off);
+          compute_chain_chunk<BITS, MT>(wlds + (p % 2) * SB::kSlot, rd_off, st[p], shift, cbc, acc);
+          load_chain_stage<BITS, MT>(st[p], ra, rbuf, voff_a, voff_b, min(c0 + i + p + P, last));
           __builtin_amdgcn_sched_barrier(0);
         }
       }
+      // the last 1..4 chunks, already loaded
+      const int r = n - i;
+#pragma unroll
+      for (int p = 0; p < P; ++p) {
+        if (p < r) {
+          if (p + 1 < r) stage_to_lds<BITS, MT>(st[(p + 1) % P], wlds + ((p + 1) % 2) * SB::kSlot, wr_off, wrap_off);
+          compute_chain_chunk<BITS, MT>(wlds + (p % 2) * SB::kSlot, rd_off, st[p], shift, cbc, acc);
+        }
+      }
     }
-    (void)s_step;
     if constexpr (CHAINED) {
       // fold this round's chains into the running sum in split order
-      __syncthreads();
+      float *pbuf = (float *)lds;                        // [kWaves][R][128]
+      __syncthreads();                                   // every wave is done with its staging
       if (active) {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
           for (int t = 0; t < 8; ++t)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) pbuf[wave][16 * mt + 4 * g + r][16 * t + c] = acc[mt][t][r];
+            for (int rr = 0; rr < 4; ++rr)
+              pbuf[(wave * R + 16 * mt + 4 * g + rr) * kBlockCols + 16 * t + c] = acc[mt][t][rr];
       }
       __syncthreads();
       const int in_round = min(kWaves, S - round * kWaves);
 #pragma unroll
       for (int e = 0; e < R * kBlockCols / kThreads; ++e) {
         const int idx = threadIdx.x + e * kThreads;
-        const int row = idx / kBlockCols, col = idx % kBlockCols;
-        float v = round == 0 ? pbuf[0][row][col] : zsum[e] + pbuf[0][row][col];
-        for (int w = 1; w < in_round; ++w) v = v + pbuf[w][row][col];
+        float v = round == 0 ? pbuf[idx] : zsum[e] + pbuf[idx];
+        for (int w = 1; w < in_round; ++w) v = v + pbuf[w * R * kBlockCols + idx];
         zsum[e] = v;
       }
     } else {
       // write this wave's split partial P_s with agent-scope stores
       if (active) {
         const int N = m.N;
-        float *P = m.partials + (int64_t)s * M * N + col0;
+        float *P_s = m.partials + (int64_t)s * M * N + col0;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
           for (int t = 0; t < 8; ++t)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int row = row_base + 16 * mt + 4 * g + r;
+            for (int rr = 0; rr < 4; ++rr) {
+              const int row = row_base + 16 * mt + 4 * g + rr;
               if (row < M)
-                __hip_atomic_store(P + (int64_t)row * N + 16 * t + c, acc[mt][t][r], __ATOMIC_RELAXED,
+                __hip_atomic_store(P_s + (int64_t)row * N + 16 * t + c, acc[mt][t][rr], __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
             }
       }
     }
   }
-  (void)z;
 
   const float sc0 = fp16_to_f32(m.scales[col0 + lane]);
   const float sc1 = fp16_to_f32(m.scales[col0 + lane + 64]);
   const float sv0 = fp16_to_f32(m.svh[col0 + lane]);
   const float sv1 = fp16_to_f32(m.svh[col0 + lane + 64]);
-  __shared__ float zrow[R][kBlockCols];
+  float *zrow = (float *)(lds + kFoldBytes);             // [R][128]
 
   if constexpr (CHAINED) {
 #pragma unroll
-    for (int e = 0; e < R * kBlockCols / kThreads; ++e) {
-      const int idx = threadIdx.x + e * kThreads;
-      zrow[idx / kBlockCols][idx % kBlockCols] = zsum[e];
-    }
+    for (int e = 0; e < R * kBlockCols / kThreads; ++e) zrow[threadIdx.x + e * kThreads] = zsum[e];
   } else {
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);             // this wave's partial stores are complete
     __syncthreads();
@@ -686,13 +726,12 @@ __global__ __launch_bounds__(kThreads) void linear_chain_kernel(const LinearArgs
       const int row = row_base + rr;
       f32x4 zv = f32x4{0.f, 0.f, 0.f, 0.f};
       if (row < M) {
-        const f32x4 *p = (const f32x4 *)(m.partials + (int64_t)row * N + col0) + c4;
+        const float *p = m.partials + (int64_t)row * N + col0 + 4 * c4;
         for (int s0 = 0; s0 < S; s0 += 8) {
           f32x4 v[8];
 #pragma unroll
           for (int u = 0; u < 8; ++u) {
-            const int sp = min(s0 + u, S - 1);
-            const float *q = (const float *)(p + (sp * split_stride) / 4);
+            const float *q = p + min(s0 + u, S - 1) * split_stride;
             v[u] = f32x4{__hip_atomic_load(q + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
                          __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
                          __hip_atomic_load(q + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
@@ -704,14 +743,15 @@ __global__ __launch_bounds__(kThreads) void linear_chain_kernel(const LinearArgs
         }
       }
 #pragma unroll
-      for (int q = 0; q < 4; ++q) zrow[rr][4 * c4 + q] = zv[q];
+      for (int q = 0; q < 4; ++q) zrow[rr * kBlockCols + 4 * c4 + q] = zv[q];
     }
   }
   __syncthreads();
   for (int rr = wave; rr < R; rr += kWaves) {
     const int row = row_base + rr;
     if (row >= M) break;
-    epilogue_row(zrow[rr][lane], zrow[rr][lane + 64], lane, sc0, sc1, sv0, sv1, m.y + (int64_t)row * m.ldy + col0);
+    epilogue_row(zrow[rr * kBlockCols + lane], zrow[rr * kBlockCols + lane + 64], lane, sc0, sc1, sv0, sv1,
+                 m.y + (int64_t)row * m.ldy + col0);
   }
 }
 
@@ -720,7 +760,8 @@ __global__ __launch_bounds__(kThreads) void linear_chain_kernel(const LinearArgs
 template <int BITS>
 __global__ __launch_bounds__(kThreads) void dequant_kernel(const DequantArgs a) {
   using T = BitsTraits<BITS>;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int C = a.K / kChunk;
   const int nb = blockIdx.x / C;
   const int chunk = blockIdx.x - nb * C;
