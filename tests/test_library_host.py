@@ -75,11 +75,19 @@ def test_plan_every_wide_n_equal(lib):
 
 
 def test_plan_table_fills_the_gpu(lib):
-    # narrow weights split until 256 workgroups or 4 chunks per split
-    for K, N in ((5120, 1024), (5120, 6144), (17408, 5120), (256, 256)):
+    """Narrow weights split until about two splits per SIMD (n_blocks * S >=
+    512), at most 16 ways, keeping >= 4 chunks per split; wide ones take
+    S_wide(K) <= 8 with >= 16 chunks per split."""
+    for K, N in ((5120, 1024), (5120, 6144), (17408, 5120), (256, 256), (1024, 384)):
         p = ex.exl3_plan(K, N, 4)
-        assert p.n_blocks * p.splits >= 256 or p.chunks // p.splits < 8 or p.splits == 32
-        assert p.chunks // p.splits >= 4
+        assert p.n_blocks < 64
+        assert p.n_blocks * p.splits >= 512 or p.splits == 16 or p.chunks // (2 * p.splits) < 4
+        assert p.chunks // p.splits >= 4 or p.splits == 1
+    for K in (1024, 5120, 17408):
+        p = ex.exl3_plan(K, 64 * 128, 4)
+        assert p.splits <= 8 and (p.chunks // p.splits >= 16 or p.splits == 1)
+    assert ex.exl3_plan(5120, 248320, 6).splits == 8
+    assert ex.exl3_plan(5120, 1024, 4).splits == 16
 
 
 def test_plan_errors(lib):

@@ -53,22 +53,26 @@ int check_weight(const exl3_weight_t *w) {
   return EXL3_OK;
 }
 
-// The plan table. S depends on (K, N, bits) only. Targets for 256 CUs:
-//  * a weight of at least EXL3_WIDE_BLOCKS blocks takes S_wide(K), so every
-//    such view plans alike; S_wide(K) = 4 once K has 32 chunks per split
-//    (K >= 4096), giving a 64-block view 256 workgroups;
-//  * a narrower weight takes the smallest power of two with n_blocks*S >= 256,
-//    at most 32 and keeping at least 4 chunks (128 K) per split.
+// The plan table. S depends on (K, N, bits) only, measured on MI355X at 1
+// and 16 rows (one K split per wave, 256 CUs):
+//  * a weight of at least EXL3_WIDE_BLOCKS blocks takes S_wide(K): the
+//    largest power of two up to 8 that keeps 16 chunks (512 K) per split, so
+//    every such view plans alike. At K = 5120 that is 8: the 64-block tail of
+//    the head then gets 512 waves, and the whole head keeps 20 chunks per
+//    wave;
+//  * a narrower weight takes the smallest power of two with n_blocks * S >=
+//    512 (about two splits per SIMD), at most 16 and keeping at least 4
+//    chunks (128 K) per split.
 int32_t splits_for(int64_t K, int64_t N, int32_t bits) {
   (void)bits;
   const int64_t chunks = K / kChunk;
   const int64_t nb = N / kBlockCols;
   int32_t s = 1;
   if (nb >= EXL3_WIDE_BLOCKS) {
-    while (s < 4 && chunks / (2 * s) >= 32) s *= 2;
+    while (s < 8 && chunks / (2 * s) >= 16) s *= 2;
     return s;
   }
-  while (nb * s < 256 && s < 32 && chunks / (2 * s) >= 4) s *= 2;
+  while (nb * s < 512 && s < 16 && chunks / (2 * s) >= 4) s *= 2;
   return s;
 }
 
@@ -99,10 +103,12 @@ Launch choose_launch(const MemberPlan *mp, int n, int64_t M) {
   if (g_hooks.chained == 0 || g_hooks.chained == 1) {
     L.chained = g_hooks.chained == 1;
   } else {
-    // partials and counters only when the grid would otherwise be too small
-    // to stream HBM: prompt row blocks and wide weights give enough
-    // workgroups by themselves.
-    L.chained = all_single || M > 128 || L.row_blocks * blocks >= 512;
+    // Partials and counters only when the grid would otherwise be too small
+    // to stream HBM: an exchange costs a few microseconds of serialized
+    // memory round trips per block (stores, counter, the last arriver's
+    // loads), which pays off below about one workgroup per CU. Prompt row
+    // blocks and wide weights give enough workgroups by themselves.
+    L.chained = all_single || M > 128 || L.row_blocks * blocks >= 256;
   }
   return L;
 }
@@ -119,7 +125,9 @@ Layout layout_for(const MemberPlan *mp, int n, int64_t M, int64_t K, const Launc
   for (int j = 0; j < n; ++j) {
     lay.xr_bytes[j] = align_up((size_t)M * K * 2);
     if (!L.chained) {
-      lay.part_bytes[j] = align_up((size_t)mp[j].splits * M * mp[j].w->N * 4);
+      // rows padded to whole row blocks (the fragment layout of the 16- and
+      // 32-row tilings stores whole 16-row tiles)
+      lay.part_bytes[j] = align_up((size_t)mp[j].splits * (L.row_blocks * 16 * L.m_tiles) * mp[j].w->N * 4);
       lay.counters += (size_t)L.row_blocks * mp[j].n_blocks;
     }
     lay.rest += lay.xr_bytes[j] + lay.part_bytes[j];

@@ -40,6 +40,10 @@ constexpr uint32_t kOutOfRange = 0x80000000u;
 // maxima (gfx9 encoding: vmcnt[3:0] bits 3:0, expcnt 6:4, lgkmcnt 11:8,
 // vmcnt[5:4] bits 15:14).
 constexpr int kWaitVmcnt0 = 0x0F70;
+// Cache policy of buffer loads and stores that exchange data between
+// workgroups: SC1, agent scope (written through / fetched past the XCD's
+// non-coherent L2), the same bit LLVM sets for agent-scope atomics here.
+constexpr int kAgentScope = 16;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, kRsrcWord3);
@@ -490,7 +494,7 @@ struct Stream {
 };
 
 template <int MT>
-struct ChainDepth { static constexpr int P = 4; };
+struct ChainDepth { static constexpr int P = 4; };   // chunks in flight per wave
 
 template <int BITS, int MT>
 struct ChainStage {
@@ -541,12 +545,18 @@ __device__ __forceinline__ void compute_chain_chunk(const char *slot, uint32_t r
   }
 }
 
+// First float of split s's partial for (row block rb, column block nb) in the
+// fragment layout [s][row block][block][MT * 8 * 256 floats].
+__device__ __forceinline__ float *partial_frag(const MemberArgs &m, int s, int rb, int nb, int row_blocks, int mt) {
+  return m.partials + (((int64_t)s * row_blocks + rb) * m.n_blocks + nb) * (int64_t)(mt * 8 * 256);
+}
+
 template <int BITS, int MT, bool CHAINED>
 __global__ __launch_bounds__(kThreads) void linear_chain_kernel(const LinearArgs a) {
   using SB = Stream<BITS>;
   constexpr int R = 16 * MT;
   constexpr int P = ChainDepth<MT>::P;
-  static_assert(P == 4, "the chunk loop unrolls by 4 = lcm(stages, LDS slots)");
+  static_assert(P % 2 == 0, "the chunk loop unrolls by P, a multiple of the 2 LDS slots");
   const int lane = threadIdx.x & 63;
   // wave index as a scalar: everything derived from it (split, chunk,
   // buffer offsets) stays in SGPRs
@@ -629,7 +639,7 @@ __global__ __launch_bounds__(kThreads) void linear_chain_kernel(const LinearArgs
         __builtin_amdgcn_sched_barrier(0);
       }
       stage_to_lds<BITS, MT>(st[0], wlds, wr_off, wrap_off);
-      // chunk i (0-based in the chain) uses VGPR stage i % 4 and LDS slot i % 2;
+      // chunk i (0-based in the chain) uses VGPR stage i % P and LDS slot i % 2;
       // the next chunk is copied to LDS before chunk i is decoded.
       int i = 0;
       for (; i + P < n; i += P) {
@@ -641,7 +651,7 @@ __global__ __launch_bounds__(kThreads) void linear_chain_kernel(const LinearArgs
           __builtin_amdgcn_sched_barrier(0);
         }
       }
-      // the last 1..4 chunks, already loaded
+      // the last 1..P chunks, already loaded
       const int r = n - i;
 #pragma unroll
       for (int p = 0; p < P; ++p) {
@@ -674,21 +684,19 @@ __global__ __launch_bounds__(kThreads) void linear_chain_kernel(const LinearArgs
         zsum[e] = v;
       }
     } else {
-      // write this wave's split partial P_s with agent-scope stores
+      // Write this wave's split partial P_s in the MFMA fragment layout
+      // [s][row block][block][mt][t][lane] x float4 (4 rows of one column),
+      // with agent-scope 128-bit stores; fragments whose 4 rows all lie past
+      // M are skipped (their rows are zero and never read).
       if (active) {
-        const int N = m.N;
-        float *P_s = m.partials + (int64_t)s * M * N + col0;
+        const __amdgpu_buffer_rsrc_t rp = make_rsrc(partial_frag(m, s, rb, nb, a.row_blocks, MT), MT * 8 * 1024);
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
           for (int t = 0; t < 8; ++t)
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-              const int row = row_base + 16 * mt + 4 * g + rr;
-              if (row < M)
-                __hip_atomic_store(P_s + (int64_t)row * N + 16 * t + c, acc[mt][t][rr], __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-            }
+            if (row_base + 16 * mt + 4 * g < M)
+              __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[mt][t]), rp,
+                                                     (mt * 8 + t) * 1024 + 16 * lane, 0, kAgentScope);
       }
     }
   }
@@ -714,36 +722,31 @@ __global__ __launch_bounds__(kThreads) void linear_chain_kernel(const LinearArgs
     __syncthreads();
     if (!s_last) return;
     if (threadIdx.x == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    // Sum the S partials in split order: every thread owns float4 columns of
-    // the block's rows; loads are issued 8 splits at a time (clamped to the
-    // last split, so the load count is static) before they are added.
-    const int N = m.N;
-    const int64_t split_stride = (int64_t)M * N;
+    // Sum the S partials in split order. Thread x owns fragments x and
+    // x + 256 (of MT * 512); their loads are issued 8 splits at a time
+    // (clamped to the last split) before they are added.
 #pragma unroll
-    for (int e = 0; e < R * kBlockCols / 4 / kThreads; ++e) {
-      const int idx = threadIdx.x + e * kThreads;        // float4 index in the block
-      const int rr = idx / (kBlockCols / 4), c4 = idx % (kBlockCols / 4);
-      const int row = row_base + rr;
-      f32x4 zv = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (row < M) {
-        const float *p = m.partials + (int64_t)row * N + col0 + 4 * c4;
+    for (int e = 0; e < MT * 2; ++e) {
+      const int f = threadIdx.x + e * kThreads;          // fragment index: mt, t, lane
+      const int fl = f & 63, ft = (f >> 6) & 7, fmt = f >> 9;
+      const int fr0 = 16 * fmt + 4 * (fl >> 4);          // first of its 4 rows in the row block
+      if (row_base + fr0 < M) {
+        f32x4 zv = f32x4{0.f, 0.f, 0.f, 0.f};
         for (int s0 = 0; s0 < S; s0 += 8) {
-          f32x4 v[8];
+          u32x4 v[8];
 #pragma unroll
           for (int u = 0; u < 8; ++u) {
-            const float *q = p + min(s0 + u, S - 1) * split_stride;
-            v[u] = f32x4{__hip_atomic_load(q + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
-                         __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
-                         __hip_atomic_load(q + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
-                         __hip_atomic_load(q + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)};
+            const __amdgpu_buffer_rsrc_t rp =
+                make_rsrc(partial_frag(m, min(s0 + u, S - 1), rb, nb, a.row_blocks, MT), MT * 8 * 1024);
+            v[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rp, 16 * f, 0, kAgentScope));
           }
 #pragma unroll
           for (int u = 0; u < 8; ++u)
-            if (s0 + u < S) zv = (s0 + u == 0) ? v[u] : zv + v[u];
+            if (s0 + u < S) zv = (s0 + u == 0) ? __builtin_bit_cast(f32x4, v[u]) : zv + __builtin_bit_cast(f32x4, v[u]);
         }
-      }
 #pragma unroll
-      for (int q = 0; q < 4; ++q) zrow[rr * kBlockCols + 4 * c4 + q] = zv[q];
+        for (int q = 0; q < 4; ++q) zrow[(fr0 + q) * kBlockCols + 16 * ft + (fl & 15)] = zv[q];
+      }
     }
   }
   __syncthreads();
