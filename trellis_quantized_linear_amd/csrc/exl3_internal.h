@@ -62,8 +62,8 @@ struct DequantArgs {
 
 // Workgroups per (row block, column block) of a launch: one when every split
 // of a block runs in one workgroup; else ceil(S / 4) for the row tilings of
-// up to 32 rows (one split per wave) and S for larger tilings (one split per
-// workgroup).
+// up to 32 rows (one split per wave) and S for the 64- and 128-row tilings
+// (one split per workgroup).
 inline int groups_per_block(int splits, int m_tiles, bool chained) {
   if (chained) return 1;
   return m_tiles <= 2 ? (splits + kWaves - 1) / kWaves : splits;

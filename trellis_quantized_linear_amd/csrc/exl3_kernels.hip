@@ -758,6 +758,264 @@ __global__ __launch_bounds__(kThreads) void linear_chain_kernel(const LinearArgs
   }
 }
 
+// ------------------------------------------------------------ linear, 128-row tiles
+//
+// Mid-M and prompt rows. A workgroup computes 128 rows x one 128-column block;
+// its 4 waves form a 2 x 2 grid of 64 x 64 tiles (4 x 4 MFMA tiles each).
+// Per 32-deep chunk the workgroup stages, with 128-bit loads, the rotated
+// input tile (128 rows x 32 K fp16, rows padded to 80 bytes so ds_read_b128
+// is conflict free) and the block's packed words (the padded tile layout of
+// the decode-row kernel) into LDS, double-buffered with one barrier per
+// chunk; global loads run 4 chunks ahead in registers. Each wave decodes its
+// 4 column tiles from the staged words and issues 16 MFMAs. Chains, their
+// fold in split order and the epilogue are those of every other tiling.
+
+template <int BITS>
+struct TileLds {
+  static constexpr int kArow = 80;                         // bytes per staged A row
+  static constexpr int kA = 128 * kArow;
+  static constexpr int kBuf = kA + Stream<BITS>::kSlot;    // one chunk: A tile + B words
+};
+
+struct TileStage {
+  u32x4 a[2];                                              // this wave's 2 A loads (32 rows)
+  u32x4 b;                                                 // this wave's B load
+};
+
+__device__ __forceinline__ void load_tile_stage(TileStage &st, __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
+                                                const uint32_t (&voff_a)[2], uint32_t voff_b, int chunk,
+                                                int chunk_bytes) {
+  st.a[0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, (int)voff_a[0], chunk * 64, 0));
+  st.a[1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, (int)voff_a[1], chunk * 64, 0));
+  st.b = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, (int)voff_b, chunk * chunk_bytes, 0));
+}
+
+template <int BITS>
+__device__ __forceinline__ void tile_stage_to_lds(const TileStage &st, char *buf, const uint32_t (&a_wr)[2],
+                                                  uint32_t b_wr, uint32_t b_wrap) {
+  *(u32x4 *)(buf + a_wr[0]) = st.a[0];
+  *(u32x4 *)(buf + a_wr[1]) = st.a[1];
+  *(u32x4 *)(buf + TileLds<BITS>::kA + b_wr) = st.b;
+  *(uint32_t *)(buf + TileLds<BITS>::kA + b_wrap) = st.b[0];
+}
+
+template <int BITS>
+__device__ __forceinline__ void compute_tile_chunk(const char *buf, const uint32_t (&a_rd)[4], uint32_t b_rd,
+                                                   uint32_t shift, const CbConst &cb, f32x4 (&acc)[4][4]) {
+  constexpr int ND = BitsTraits<BITS>::kDwords;
+  half8 af[4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) af[mt] = __builtin_bit_cast(half8, *(const u32x4 *)(buf + a_rd[mt]));
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t *q = (const uint32_t *)(buf + TileLds<BITS>::kA + b_rd + i * Stream<BITS>::kStride);
+    uint32_t w[ND];
+#pragma unroll
+    for (int d = 0; d < ND; ++d) w[d] = q[d];
+    const half8 bf = decode8<BITS>(w, shift, cb);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+      acc[mt][i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[mt], bf, acc[mt][i], 0, 0, 0);
+  }
+}
+
+template <int BITS, bool CHAINED>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void linear_tile_kernel(const LinearArgs a) {
+  using SB = Stream<BITS>;
+  using TL = TileLds<BITS>;
+  constexpr int R = 128;
+  constexpr int P = 4;                                     // register stages (chunks in flight)
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wr = wave >> 1, wc = wave & 1;
+  const int bid = blockIdx.x;
+  int j = 0;
+  if (a.n_members > 1 && bid >= a.m[1].wg_begin) j = 1;
+  if (a.n_members > 2 && bid >= a.m[2].wg_begin) j = 2;
+  const MemberArgs &m = a.m[j];
+  const int S = m.splits;
+  const int groups = m.groups;                             // 1 (chained) or S
+  const int local = bid - m.wg_begin;
+  const int per_rb = m.n_blocks * groups;
+  const int rb = local / per_rb;
+  const int rem = local - rb * per_rb;
+  const int nb = rem / groups;
+  const int sg = rem - nb * groups;
+  const int M = a.M, K = a.K, C = a.chunks;
+  const int row_base = rb * R;
+  const int col0 = nb * kBlockCols;
+
+  constexpr int kStage = 2 * TL::kBuf;
+  constexpr int kEpi = 16 * 132 * 4;
+  __shared__ __attribute__((aligned(16))) char lds[kStage > kEpi ? kStage : kEpi];
+
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(m.xr, (uint32_t)((uint64_t)M * K * 2));
+  const __amdgpu_buffer_rsrc_t rbuf = make_rsrc(m.words + (int64_t)nb * m.block_stride, (uint32_t)(16u * K * BITS));
+  const int c = lane & 15, g = lane >> 4;
+
+  // staging: wave w loads A rows 32w .. 32w+31 (16 per 128-bit load, 4 lanes
+  // a row) and, if w < kLoads, the w-th 1 KB of the chunk's words (other
+  // waves and lanes past the chunk load its first bytes into the dump)
+  uint32_t voff_a[2], a_wr[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = 32 * wave + 16 * i + (lane >> 2);
+    const int row = row_base + r;
+    voff_a[i] = row < M ? (uint32_t)(row * 2 * K + 16 * (lane & 3)) : kOutOfRange;
+    a_wr[i] = (uint32_t)(r * TL::kArow + 16 * (lane & 3));
+  }
+  const int boff = 1024 * wave + 16 * lane;
+  const bool bvalid = wave < SB::kLoads && boff < SB::kChunkBytes;
+  const int tau_w = boff / (32 * BITS), w_in = boff % (32 * BITS);
+  const uint32_t voff_b = bvalid ? (uint32_t)boff : 0u;
+  const uint32_t b_wr = bvalid ? (uint32_t)(tau_w * SB::kStride + w_in) : (uint32_t)(16 * SB::kStride);
+  const uint32_t b_wrap =
+      bvalid ? (uint32_t)(tau_w * SB::kStride + 32 * BITS + (w_in == 0 ? 0 : 4)) : (uint32_t)(16 * SB::kStride);
+  // reading: A fragments of m-tiles 4wr..4wr+3, B words of column tiles 4wc..4wc+3
+  uint32_t a_rd[4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) a_rd[mt] = (uint32_t)((64 * wr + 16 * mt + c) * TL::kArow + 16 * g);
+  const int jseg = 2 * c + (g & 1);
+  const uint32_t shift = 8u * (uint32_t)((BITS * jseg) & 3);
+  const uint32_t b_rd = (uint32_t)(((g >> 1) * 8 + 4 * wc) * SB::kStride + 4 * ((BITS * jseg) >> 2));
+  const CbConst cbc = cb_const();
+
+  // chunk range: all splits (chained) or split sg
+  const int s_begin = CHAINED ? 0 : sg;
+  const int cb = (int)(((int64_t)s_begin * C) / S);
+  const int ce = (int)(((int64_t)(CHAINED ? S : sg + 1) * C) / S);
+  const int n = ce - cb;
+  const int last = ce - 1;
+  int s = s_begin;
+  int bnd = (int)(((int64_t)(s + 1) * C) / S);             // end of the current chain
+
+  f32x4 acc[4][4];
+  f32x4 z[4][4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[mt][i] = z[mt][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  TileStage st[P];
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+    load_tile_stage(st[p], ra, rbuf, voff_a, voff_b, min(cb + p, last), SB::kChunkBytes);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  tile_stage_to_lds<BITS>(st[0], lds, a_wr, b_wr, b_wrap);
+
+  // one step: chunk cc from LDS buffer `cur`; chunk cc+1 is staged into the
+  // other buffer first; the register stage of chunk cc reloads chunk cc+P
+  auto step = [&](int cc, char *cur, char *nxt, TileStage &mine, TileStage &next, bool has_next) {
+    __syncthreads();
+    if (has_next) tile_stage_to_lds<BITS>(next, nxt, a_wr, b_wr, b_wrap);
+    load_tile_stage(mine, ra, rbuf, voff_a, voff_b, min(cc + P, last), SB::kChunkBytes);
+    compute_tile_chunk<BITS>(cur, a_rd, b_rd, shift, cbc, acc);
+    if (cc + 1 == bnd) {                                   // chain s complete (uniform)
+      if constexpr (CHAINED) {
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            z[mt][i] = (s == 0) ? acc[mt][i] : z[mt][i] + acc[mt][i];
+            acc[mt][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+          }
+      }
+      ++s;
+      bnd = (int)(((int64_t)(s + 1) * C) / S);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  int i = 0;
+  for (; i + P < n; i += P) {
+#pragma unroll
+    for (int p = 0; p < P; ++p)
+      step(cb + i + p, lds + (p % 2) * TL::kBuf, lds + ((p + 1) % 2) * TL::kBuf, st[p], st[(p + 1) % P], true);
+  }
+  const int r = n - i;
+#pragma unroll
+  for (int p = 0; p < P; ++p)
+    if (p < r)
+      step(cb + i + p, lds + (p % 2) * TL::kBuf, lds + ((p + 1) % 2) * TL::kBuf, st[p], st[(p + 1) % P], p + 1 < r);
+
+  const float sc0 = fp16_to_f32(m.scales[col0 + lane]);
+  const float sc1 = fp16_to_f32(m.scales[col0 + lane + 64]);
+  const float sv0 = fp16_to_f32(m.svh[col0 + lane]);
+  const float sv1 = fp16_to_f32(m.svh[col0 + lane + 64]);
+  float *zbuf = (float *)lds;                              // [16][132] per m-tile pass
+
+  if constexpr (!CHAINED) {
+    // split sg's partial in the fragment layout, then the counter exchange
+    const __amdgpu_buffer_rsrc_t rp = make_rsrc(partial_frag(m, sg, rb, nb, a.row_blocks, 8), 8 * 8 * 1024);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int i2 = 0; i2 < 4; ++i2)
+        if (row_base + 64 * wr + 16 * mt + 4 * g < M)
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[mt][i2]), rp,
+                                                 ((4 * wr + mt) * 8 + 4 * wc + i2) * 1024 + 16 * lane, 0,
+                                                 kAgentScope);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+    __shared__ int s_last;
+    uint32_t *counter = m.counters + (int64_t)rb * m.n_blocks + nb;
+    if (threadIdx.x == 0) {
+      const uint32_t prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_last = prev == (uint32_t)(groups - 1);
+    }
+    __syncthreads();
+    if (!s_last) return;
+    if (threadIdx.x == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // z = P0 + P1 + ... for this wave's own 16 fragments, 4 splits per batch
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int i2 = 0; i2 < 4; ++i2) {
+        const int f = ((4 * wr + mt) * 8 + 4 * wc + i2) * 64 + lane;
+        if (row_base + 64 * wr + 16 * mt + 4 * g < M) {
+          f32x4 zv = f32x4{0.f, 0.f, 0.f, 0.f};
+          for (int s0 = 0; s0 < S; s0 += 4) {
+            u32x4 v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              const __amdgpu_buffer_rsrc_t rq =
+                  make_rsrc(partial_frag(m, min(s0 + u, S - 1), rb, nb, a.row_blocks, 8), 8 * 8 * 1024);
+              v[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, 16 * f, 0, kAgentScope));
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+              if (s0 + u < S)
+                zv = (s0 + u == 0) ? __builtin_bit_cast(f32x4, v[u]) : zv + __builtin_bit_cast(f32x4, v[u]);
+          }
+          z[mt][i2] = zv;
+        }
+      }
+  }
+
+  // epilogue, one 16-row m-tile at a time through LDS
+#pragma unroll
+  for (int mtg = 0; mtg < 8; ++mtg) {
+    const int row0 = row_base + 16 * mtg;
+    if (row0 >= M) break;                                  // uniform
+    __syncthreads();
+    if (wr == (mtg >> 2)) {
+#pragma unroll
+      for (int i2 = 0; i2 < 4; ++i2)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) zbuf[(4 * g + q) * 132 + 16 * (4 * wc + i2) + c] = z[mtg & 3][i2][q];
+    }
+    __syncthreads();
+    for (int rr = wave; rr < 16; rr += kWaves) {
+      const int row = row0 + rr;
+      if (row < M)
+        epilogue_row(zbuf[rr * 132 + lane], zbuf[rr * 132 + lane + 64], lane, sc0, sc1, sv0, sv1,
+                     m.y + (int64_t)row * m.ldy + col0);
+    }
+  }
+}
+
 // ------------------------------------------------------------ test hooks
 
 template <int BITS>
@@ -814,7 +1072,7 @@ constexpr LinearFn pick_mt(int mti) {
   return mti == 0 ? linear_chain_kernel<BITS, 1, CHAINED>
        : mti == 1 ? linear_chain_kernel<BITS, 2, CHAINED>
        : mti == 2 ? linear_ntile_kernel<BITS, 4, CHAINED>
-                  : linear_ntile_kernel<BITS, 8, CHAINED>;
+                  : linear_tile_kernel<BITS, CHAINED>;
 }
 
 template <int BITS>
