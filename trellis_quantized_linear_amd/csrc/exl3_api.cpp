@@ -84,9 +84,15 @@ struct MemberPlan {
 
 struct Launch {
   int m_tiles;
+  int kernel;               // exl3::LinearKernel
   bool chained;
   int64_t row_blocks;
 };
+
+// Decode rows (up to 16): at or above this many blocks, one 8-wave workgroup
+// per block (chained splits, two workgroups per CU) keeps every CU busy
+// without partials; below it, K splits exchange partials across workgroups.
+constexpr int64_t kChainedMinBlocks16 = 256;
 
 Launch choose_launch(const MemberPlan *mp, int n, int64_t M) {
   Launch L;
@@ -102,6 +108,8 @@ Launch choose_launch(const MemberPlan *mp, int n, int64_t M) {
   }
   if (g_hooks.chained == 0 || g_hooks.chained == 1) {
     L.chained = g_hooks.chained == 1;
+  } else if (mt == 1) {
+    L.chained = all_single || blocks >= kChainedMinBlocks16;
   } else {
     // Partials and counters only when the grid would otherwise be too small
     // to stream HBM: an exchange costs a few microseconds of serialized
@@ -110,6 +118,10 @@ Launch choose_launch(const MemberPlan *mp, int n, int64_t M) {
     // blocks and wide weights give enough workgroups by themselves.
     L.chained = all_single || M > 128 || L.row_blocks * blocks >= 256;
   }
+  L.kernel = mt == 1 ? (L.chained ? exl3::kChain16x8 : exl3::kChain16)
+           : mt == 2 ? exl3::kChain32
+           : mt == 4 ? exl3::kNtile64
+                     : exl3::kTile128;
   return L;
 }
 
@@ -293,7 +305,7 @@ int run_group(int32_t n_members, const exl3_weight_t *const *w, const void *x, i
     m.N = (int32_t)wj->N;
     m.n_blocks = mp[j].n_blocks;
     m.splits = mp[j].splits;
-    m.groups = exl3::groups_per_block(mp[j].splits, L.m_tiles, L.chained);
+    m.groups = exl3::groups_per_block(mp[j].splits, L.kernel, L.chained);
     m.wg_begin = (int32_t)wg;
     if (!L.chained) {
       m.partials = (float *)(base + off);
@@ -327,7 +339,7 @@ int run_group(int32_t n_members, const exl3_weight_t *const *w, const void *x, i
     if (e) return hip_fail(e);
   }
   if (phases & kLinear) {
-    e = exl3::launch_linear(la, w[0]->bits, L.m_tiles, L.chained, stream);
+    e = exl3::launch_linear(la, w[0]->bits, L.kernel, L.chained, stream);
     if (e) return hip_fail(e);
   }
   return EXL3_OK;

@@ -60,17 +60,29 @@ struct DequantArgs {
   int32_t N;
 };
 
-// Workgroups per (row block, column block) of a launch: one when every split
-// of a block runs in one workgroup; else ceil(S / 4) for the row tilings of
-// up to 32 rows (one split per wave) and S for the 64- and 128-row tilings
-// (one split per workgroup).
-inline int groups_per_block(int splits, int m_tiles, bool chained) {
+// Linear kernels.
+enum LinearKernel {
+  kChain16 = 0,     // 16 rows, 4 waves per workgroup, one split per wave
+  kChain16x8 = 1,   // 16 rows, 8 waves per workgroup, all splits of a block (chained only)
+  kChain32 = 2,     // 32 rows, 4 waves per workgroup, one split per wave
+  kNtile64 = 3,     // 64 rows per workgroup, waves own column tiles
+  kTile128 = 4,     // 128 rows per workgroup, 2 x 2 waves of 64 x 64
+};
+
+inline int waves_per_wg(int kernel) { return kernel == kChain16x8 ? 8 : kWaves; }
+inline int threads_per_wg(int kernel) { return 64 * waves_per_wg(kernel); }
+
+// Arrivals per (row block, column block) of a launch: one when every split of
+// a block runs in one workgroup; else ceil(S / W) workgroups for the 16- and
+// 32-row tilings (one split per wave, W waves) and S for the 64- and 128-row
+// tilings (one split per workgroup).
+inline int groups_per_block(int splits, int kernel, bool chained) {
   if (chained) return 1;
-  return m_tiles <= 2 ? (splits + kWaves - 1) / kWaves : splits;
+  return kernel <= kChain32 ? (splits + waves_per_wg(kernel) - 1) / waves_per_wg(kernel) : splits;
 }
 
 // Launchers (exl3_kernels.hip). Each returns a hipError_t as int.
-int launch_linear(const LinearArgs &a, int bits, int m_tiles, bool chained, void *stream);
+int launch_linear(const LinearArgs &a, int bits, int kernel, bool chained, void *stream);
 int launch_rot(const RotArgs &a, void *stream);
 int launch_dequant(const DequantArgs &a, int bits, void *stream);
 int launch_codebook(const uint16_t *states, uint16_t *out, int64_t n, void *stream);

@@ -181,14 +181,6 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t u) { return __uint_as_floa
 __device__ __forceinline__ float fp16_to_f32(uint16_t u) { return (float)__builtin_bit_cast(_Float16, u); }
 __device__ __forceinline__ uint16_t f32_to_fp16(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
 
-// fp32 -> bf16, round to nearest even; NaN stays NaN (quieted).
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x0040u);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
-
 // ------------------------------------------------------------ Hadamard
 // Unnormalised 128-point Sylvester transform of one 128-vector held by a wave,
 // element `lane` in v0 and element `lane + 64` in v1. Levels h = 1, 2, ..., 64
@@ -206,17 +198,158 @@ __device__ __forceinline__ void fwht128_pair(float &v0, float &v1, int lane) {
   v1 = a - b;
 }
 
-// Epilogue of one output row of one 128-column block: scale, output Hadamard,
-// 2^-3, output signs, bf16. The one routine every regime uses.
-__device__ __forceinline__ void epilogue_row(float z0, float z1, int lane, float sc0, float sc1,
-                                             float sv0, float sv1, uint16_t *yrow) {
-  float v0 = z0 * sc0;
-  float v1 = z1 * sc1;
-  fwht128_pair(v0, v1, lane);
-  v0 = (v0 * 0.125f) * sv0;
-  v1 = (v1 * 0.125f) * sv1;
-  yrow[lane] = f32_to_bf16(v0);
-  yrow[lane + 64] = f32_to_bf16(v1);
+// ------------------------------------------------------------ epilogue
+//
+// A wave finishes 4*NQ rows of one block's Z (rows row0 .. row0 + 4NQ - 1,
+// columns col0 .. col0 + 127): lane l, with c = l % 16 and g = l / 16, holds
+// z[t][q] = Z[row0 + NQ*g + q][col0 + 16t + c]. With NQ = 4 that is the MFMA
+// accumulator layout of a 16-row tile. Per column: times its scale, the
+// unnormalised 128-point Sylvester transform by levels h = 1, 2, 4, ..., 64
+// in that order (each pair (i, i + h) becomes (a + b, a - b) in fp32), times
+// 2^-3 and the column's output sign, then bf16 with round to nearest even.
+// The same arithmetic runs in every row regime.
+//
+// Column bits 0..3 are lane bits: levels 1, 2, 4 and 8 pair lanes c and c ^ h
+// of one 16-lane DPP row. Column bits 4..6 are register bits: levels 16, 32
+// and 64 pair registers t and t ^ (h / 16). The bf16 rows pass through NQ KB
+// of LDS owned by the wave (`scratch`) so that each lane stores 16
+// contiguous bytes of a row.
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Value of lane (c ^ H) of the lane's 16-lane row.
+template <int H>
+__device__ __forceinline__ float row_xor(float v) {
+  int x = __float_as_int(v);
+  if constexpr (H == 1) {
+    x = __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, true);      // quad_perm [1,0,3,2]
+  } else if constexpr (H == 2) {
+    x = __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, true);      // quad_perm [2,3,0,1]
+  } else if constexpr (H == 4) {
+    x = __builtin_amdgcn_mov_dpp(x, 0x141, 0xF, 0xF, true);     // row_half_mirror: c ^ 7
+    x = __builtin_amdgcn_mov_dpp(x, 0x1B, 0xF, 0xF, true);      // quad_perm [3,2,1,0]: ^ 3
+  } else {
+    static_assert(H == 8, "lane levels are 1, 2, 4 and 8");
+    x = __builtin_amdgcn_mov_dpp(x, 0x128, 0xF, 0xF, true);     // row_ror:8
+  }
+  return __int_as_float(x);
+}
+
+// One lane level: the lower lane of a pair keeps a + b, the upper one a - b.
+// With sgn = +1 (lower) or -1 (upper), fma(sgn, v, partner) rounds once, as
+// v + partner or partner - v would.
+template <int H, int NQ>
+__device__ __forceinline__ void lane_level(float (&z)[8][NQ], int c) {
+  const float sgn = (c & H) ? -1.0f : 1.0f;
+#pragma unroll
+  for (int t = 0; t < 8; ++t)
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) z[t][q] = __builtin_fmaf(sgn, z[t][q], row_xor<H>(z[t][q]));
+}
+
+template <int K, int NQ>
+__device__ __forceinline__ void register_level(float (&z)[8][NQ]) {
+#pragma unroll
+  for (int t = 0; t < 8; ++t)
+    if ((t & K) == 0) {
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) {
+        const float a = z[t][q], b = z[t + K][q];
+        z[t][q] = a + b;
+        z[t + K][q] = a - b;
+      }
+    }
+}
+
+// The lane's column constants: scales and 2^-3 * output signs of columns
+// col0 + 16t + c. (v * 2^-3) * svh == v * (2^-3 * svh): the first product is
+// exact. Loaded ahead of the epilogue to hide their latency.
+struct EpiCols {
+  float sc[8], so[8];
+};
+
+__device__ __forceinline__ EpiCols epi_cols(const MemberArgs &m, int col0, int lane) {
+  const int c = lane & 15;
+  EpiCols e;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    e.sc[t] = fp16_to_f32(m.scales[col0 + 16 * t + c]);
+    e.so[t] = 0.125f * fp16_to_f32(m.svh[col0 + 16 * t + c]);
+  }
+  return e;
+}
+
+__device__ __forceinline__ void wave_lds_sync() {
+  // a wave's LDS accesses complete in order; keep the compiler from moving
+  // the reads of other lanes' writes above them
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <int NQ>
+__device__ __forceinline__ void epilogue_rows(float (&z)[8][NQ], const EpiCols &ec, int lane, const MemberArgs &m,
+                                              int col0, int row0, int M, uint16_t *scratch) {
+  const int c = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int t = 0; t < 8; ++t)
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) z[t][q] = z[t][q] * ec.sc[t];
+  lane_level<1>(z, c);
+  lane_level<2>(z, c);
+  lane_level<4>(z, c);
+  lane_level<8>(z, c);
+  register_level<1>(z);
+  register_level<2>(z);
+  register_level<4>(z);
+  // bf16 (v_cvt_pk_bf16_f32: round to nearest even, NaN stays NaN), two
+  // columns 16 apart per conversion, into scratch[row][column]
+#pragma unroll
+  for (int t = 0; t < 8; t += 2)
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      const bf16x2 h = __builtin_convertvector(f32x2{z[t][q] * ec.so[t], z[t + 1][q] * ec.so[t + 1]}, bf16x2);
+      const uint32_t u = __builtin_bit_cast(uint32_t, h);
+      uint16_t *row = scratch + (NQ * g + q) * kBlockCols;
+      row[16 * t + c] = (uint16_t)(u & 0xFFFFu);
+      row[16 * t + 16 + c] = (uint16_t)(u >> 16);
+    }
+  wave_lds_sync();
+#pragma unroll
+  for (int i = 0; i < NQ; ++i) {
+    const int piece = lane + 64 * i;                  // 16 bytes: row piece/16, columns 8*(piece%16) ..
+    const int r = piece >> 4, cc = 8 * (piece & 15);
+    if (row0 + r < M) {
+      const u32x4 v = *(const u32x4 *)(scratch + r * kBlockCols + cc);
+      uint16_t *dst = m.y + (int64_t)(row0 + r) * m.ldy + col0 + cc;
+      if (((uintptr_t)dst & 15) == 0) {
+        *(u32x4 *)dst = v;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          dst[2 * e] = (uint16_t)(v[e] & 0xFFFFu);
+          dst[2 * e + 1] = (uint16_t)(v[e] >> 16);
+        }
+      }
+    }
+  }
+}
+
+// Rows row0 .. row0 + 4NQ - 1 of a block's Z from LDS (row pitch `pitch`
+// floats; rows past M may hold anything) through the epilogue. The rows'
+// LDS doubles as the wave's bf16 scratch once they are in registers.
+template <int NQ>
+__device__ __forceinline__ void epilogue_rows_lds(float *zrows, int pitch, const EpiCols &ec, int lane,
+                                                  const MemberArgs &m, int col0, int row0, int M) {
+  const int c = lane & 15, g = lane >> 4;
+  float z[8][NQ];
+#pragma unroll
+  for (int t = 0; t < 8; ++t)
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) z[t][q] = zrows[(NQ * g + q) * pitch + 16 * t + c];
+  wave_lds_sync();
+  epilogue_rows<NQ>(z, ec, lane, m, col0, row0, M, (uint16_t *)zrows);
 }
 
 // Position of logical K index k inside its 8-group in slot order:
@@ -390,30 +523,15 @@ __global__ __launch_bounds__(kThreads) void linear_ntile_kernel(const LinearArgs
     }
   }
 
-  const float sc0 = fp16_to_f32(m.scales[col0 + lane]);
-  const float sc1 = fp16_to_f32(m.scales[col0 + lane + 64]);
-  const float sv0 = fp16_to_f32(m.svh[col0 + lane]);
-  const float sv1 = fp16_to_f32(m.svh[col0 + lane + 64]);
-
+  __shared__ float zbuf[R][132];
+  const EpiCols ec = epi_cols(m, col0, lane);
   if constexpr (CHAINED) {
-    __shared__ float zbuf[16][132];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const int row0 = row_base + 16 * mt;
-      if (row0 >= M) break;                         // uniform
-      __syncthreads();
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) zbuf[4 * g + r][16 * (2 * wave + i) + c] = z[mt][i][r];
-      __syncthreads();
-      for (int rr = wave; rr < 16; rr += kWaves) {
-        const int row = row0 + rr;
-        if (row < M)
-          epilogue_row(zbuf[rr][lane], zbuf[rr][lane + 64], lane, sc0, sc1, sv0, sv1,
-                       m.y + (int64_t)row * m.ldy + col0);
-      }
-    }
+        for (int r = 0; r < 4; ++r) zbuf[16 * mt + 4 * g + r][16 * (2 * wave + i) + c] = z[mt][i][r];
   } else {
     // Write this split's fp32 partial P_s[row][col] with agent-scope stores
     // (written through the XCD's non-coherent L2), wait until every wave's
@@ -459,19 +577,25 @@ __global__ __launch_bounds__(kThreads) void linear_ntile_kernel(const LinearArgs
         z0 = z0 + __hip_atomic_load(p + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         z1 = z1 + __hip_atomic_load(p + lane + 64, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
-      epilogue_row(z0, z1, lane, sc0, sc1, sv0, sv1, m.y + (int64_t)row * m.ldy + col0);
+      zbuf[rr][lane] = z0;
+      zbuf[rr][lane + 64] = z1;
     }
   }
+  __syncthreads();
+  if (wave < MT && row_base + 16 * wave < M)
+    epilogue_rows_lds<4>(&zbuf[16 * wave][0], 132, ec, lane, m, col0, row_base + 16 * wave, M);
 }
 
 
 // ------------------------------------------------------------ linear, one split per wave
 //
-// Row tilings of 16 and 32 rows. Wave w of a workgroup runs whole K-split
-// chains over all 8 column tiles of the block, so one A fragment (the rotated
-// input, 16 rows x 32 K) feeds 8 MFMAs. Chains are assigned round-robin: when
-// the workgroup owns every split of its block (chained), wave w runs splits w,
-// w+4, ...; otherwise workgroup g owns splits 4g..4g+3, one per wave.
+// Row tilings of 16 and 32 rows, W waves per workgroup. Wave w runs whole
+// K-split chains over all 8 column tiles of the block, so one A fragment (the
+// rotated input, 16 rows x 32 K) feeds 8 MFMAs. Chains are assigned
+// round-robin: when the workgroup owns every split of its block (chained),
+// wave w runs splits w, w+W, ... and the workgroup folds them in split order
+// in LDS; otherwise workgroup g owns splits Wg .. Wg+W-1, one per wave, and
+// the split partials meet through the workspace.
 //
 // Weight stream. A chunk of a block is two tile rows of 8 tiles, 512*b
 // contiguous bytes. Each wave fetches its chunks with 128-bit loads (b/2
@@ -551,12 +675,102 @@ __device__ __forceinline__ float *partial_frag(const MemberArgs &m, int s, int r
   return m.partials + (((int64_t)s * row_blocks + rb) * m.n_blocks + nb) * (int64_t)(mt * 8 * 256);
 }
 
-template <int BITS, int MT, bool CHAINED>
-__global__ __launch_bounds__(kThreads) void linear_chain_kernel(const LinearArgs a) {
+// Per-wave constants of the chain loop: buffer resources, lane offsets of
+// the A loads, the 128-bit B loads and their LDS slots, and the lane's read
+// offset and bit shift in a staged chunk.
+template <int BITS, int MT>
+struct ChainCtx {
+  __amdgpu_buffer_rsrc_t ra, rb;
+  uint32_t voff_a[MT];
+  uint32_t voff_b[Stream<BITS>::kLoads], wr_off[Stream<BITS>::kLoads], wrap_off[Stream<BITS>::kLoads];
+  uint32_t rd_off, shift;
+  CbConst cb;
+};
+
+template <int BITS, int MT>
+__device__ __forceinline__ ChainCtx<BITS, MT> chain_ctx(const MemberArgs &m, int M, int K, int nb, int row_base,
+                                                       int lane) {
+  using SB = Stream<BITS>;
+  ChainCtx<BITS, MT> x;
+  x.ra = make_rsrc(m.xr, (uint32_t)((uint64_t)M * K * 2));
+  x.rb = make_rsrc(m.words + (int64_t)nb * m.block_stride, (uint32_t)(16u * K * BITS));
+  const int c = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int row = row_base + 16 * mt + c;
+    x.voff_a[mt] = row < M ? (uint32_t)(row * 2 * K + 16 * g) : kOutOfRange;
+  }
+  // 128-bit load l covers chunk bytes [1024 l, 1024 l + 1024); lane bytes
+  // 16 lane .. +15 of it belong to one tile (tiles are 32b bytes, a multiple
+  // of 16). Lanes past the chunk's end load its first bytes and dump them.
+#pragma unroll
+  for (int l = 0; l < SB::kLoads; ++l) {
+    const int off = 1024 * l + 16 * lane;
+    const bool valid = off < SB::kChunkBytes;
+    const int tau = off / (32 * BITS), w = off % (32 * BITS);
+    x.voff_b[l] = valid ? (uint32_t)off : 0u;
+    x.wr_off[l] = valid ? (uint32_t)(tau * SB::kStride + w) : (uint32_t)(16 * SB::kStride);
+    x.wrap_off[l] = valid ? (uint32_t)(tau * SB::kStride + 32 * BITS + (w == 0 ? 0 : 4)) : (uint32_t)(16 * SB::kStride);
+  }
+  const int jseg = 2 * c + (g & 1);
+  x.shift = 8u * (uint32_t)((BITS * jseg) & 3);
+  x.rd_off = (uint32_t)((g >> 1) * 8 * SB::kStride + 4 * ((BITS * jseg) >> 2));
+  x.cb = cb_const();
+  return x;
+}
+
+// One K-split chain: chunks [c0, c1) of the block over all 8 column tiles and
+// MT 16-row tiles, accumulated from zero in ascending chunk order. Chunk i of
+// the chain uses register stage i % P and LDS slot i % 2 of the wave's
+// region `wlds`; the next chunk is copied to LDS before chunk i is decoded.
+template <int BITS, int MT, int P>
+__device__ __forceinline__ void run_chain(f32x4 (&acc)[MT][8], int c0, int c1, char *wlds,
+                                          const ChainCtx<BITS, MT> &x) {
+  using SB = Stream<BITS>;
+  static_assert(P % 2 == 0, "the chunk loop unrolls by P, a multiple of the 2 LDS slots");
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int t = 0; t < 8; ++t) acc[mt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int n = c1 - c0;
+  const int last = c1 - 1;
+  ChainStage<BITS, MT> st[P];
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+    load_chain_stage<BITS, MT>(st[p], x.ra, x.rb, x.voff_a, x.voff_b, min(c0 + p, last));
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  stage_to_lds<BITS, MT>(st[0], wlds, x.wr_off, x.wrap_off);
+  int i = 0;
+  for (; i + P < n; i += P) {
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      stage_to_lds<BITS, MT>(st[(p + 1) % P], wlds + ((p + 1) % 2) * SB::kSlot, x.wr_off, x.wrap_off);
+      compute_chain_chunk<BITS, MT>(wlds + (p % 2) * SB::kSlot, x.rd_off, st[p], x.shift, x.cb, acc);
+      load_chain_stage<BITS, MT>(st[p], x.ra, x.rb, x.voff_a, x.voff_b, min(c0 + i + p + P, last));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  // the last 1..P chunks, already loaded
+  const int r = n - i;
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+    if (p < r) {
+      if (p + 1 < r) stage_to_lds<BITS, MT>(st[(p + 1) % P], wlds + ((p + 1) % 2) * SB::kSlot, x.wr_off, x.wrap_off);
+      compute_chain_chunk<BITS, MT>(wlds + (p % 2) * SB::kSlot, x.rd_off, st[p], x.shift, x.cb, acc);
+    }
+  }
+}
+
+// ------------------------------------------------------------ linear, 16 and 32 rows per workgroup
+
+// W = 8 (chained, 16 rows) keeps to 128 VGPRs so that two workgroups fit a CU.
+template <int BITS, int MT, bool CHAINED, int W>
+__global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(W == 8 ? 4 : 1)))
+void linear_chain_kernel(const LinearArgs a) {
   using SB = Stream<BITS>;
   constexpr int R = 16 * MT;
-  constexpr int P = ChainDepth<MT>::P;
-  static_assert(P % 2 == 0, "the chunk loop unrolls by P, a multiple of the 2 LDS slots");
+  constexpr int NT = W * 64;                             // threads
   const int lane = threadIdx.x & 63;
   // wave index as a scalar: everything derived from it (split, chunk,
   // buffer offsets) stays in SGPRs
@@ -580,90 +794,33 @@ __global__ __launch_bounds__(kThreads) void linear_chain_kernel(const LinearArgs
 
   // LDS: per-wave weight staging during the chunk loops; afterwards the
   // same bytes hold the chain fold buffers and the epilogue rows.
-  constexpr int kStageBytes = kWaves * SB::kWave;
-  constexpr int kFoldBytes = (CHAINED ? kWaves : 0) * R * kBlockCols * 4;
+  constexpr int kStageBytes = W * SB::kWave;
+  constexpr int kFoldBytes = (CHAINED ? W : 0) * R * kBlockCols * 4;
   constexpr int kRowBytes = R * kBlockCols * 4;
   constexpr int kLds = kStageBytes > kFoldBytes + kRowBytes ? kStageBytes : kFoldBytes + kRowBytes;
   __shared__ __attribute__((aligned(16))) char lds[kLds];
   char *wlds = lds + wave * SB::kWave;
 
-  const __amdgpu_buffer_rsrc_t ra = make_rsrc(m.xr, (uint32_t)((uint64_t)M * K * 2));
-  const __amdgpu_buffer_rsrc_t rbuf = make_rsrc(m.words + (int64_t)nb * m.block_stride, (uint32_t)(16u * K * BITS));
+  const ChainCtx<BITS, MT> x = chain_ctx<BITS, MT>(m, M, K, nb, row_base, lane);
   const int c = lane & 15, g = lane >> 4;
-  uint32_t voff_a[MT];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const int row = row_base + 16 * mt + c;
-    voff_a[mt] = row < M ? (uint32_t)(row * 2 * K + 16 * g) : kOutOfRange;
-  }
-  // 128-bit load l covers chunk bytes [1024 l, 1024 l + 1024); lane bytes
-  // 16 lane .. +15 of it belong to one tile (tiles are 32b bytes, a multiple
-  // of 16). Lanes past the chunk's end load its first bytes and dump them.
-  uint32_t voff_b[SB::kLoads], wr_off[SB::kLoads], wrap_off[SB::kLoads];
-#pragma unroll
-  for (int l = 0; l < SB::kLoads; ++l) {
-    const int off = 1024 * l + 16 * lane;
-    const bool valid = off < SB::kChunkBytes;
-    const int tau = off / (32 * BITS), w = off % (32 * BITS);
-    voff_b[l] = valid ? (uint32_t)off : 0u;
-    wr_off[l] = valid ? (uint32_t)(tau * SB::kStride + w) : (uint32_t)(16 * SB::kStride);
-    wrap_off[l] = valid ? (uint32_t)(tau * SB::kStride + 32 * BITS + (w == 0 ? 0 : 4)) : (uint32_t)(16 * SB::kStride);
-  }
-  const int jseg = 2 * c + (g & 1);
-  const uint32_t shift = 8u * (uint32_t)((BITS * jseg) & 3);
-  const uint32_t rd_off = (uint32_t)((g >> 1) * 8 * SB::kStride + 4 * ((BITS * jseg) >> 2));
-  const CbConst cbc = cb_const();
 
-  const int s_first = CHAINED ? wave : kWaves * sg + wave;
-  const int rounds = CHAINED ? (S + kWaves - 1) / kWaves : 1;
-  float zsum[CHAINED ? R * kBlockCols / kThreads : 1];
+  const int s_first = CHAINED ? wave : W * sg + wave;
+  const int rounds = CHAINED ? (S + W - 1) / W : 1;
+  float zsum[CHAINED ? R * kBlockCols / NT : 1];
 
   for (int round = 0; round < rounds; ++round) {
-    const int s = s_first + round * (CHAINED ? kWaves : 0);
+    const int s = s_first + round * (CHAINED ? W : 0);
     const bool active = s < S;                           // uniform per wave
     f32x4 acc[MT][8];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int t = 0; t < 8; ++t) acc[mt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (CHAINED && round > 0) __syncthreads();           // fold buffers of the last round are read
     if (active) {
-      const int c0 = (int)(((int64_t)s * C) / S);
-      const int c1 = (int)(((int64_t)(s + 1) * C) / S);
-      const int n = c1 - c0;
-      const int last = c1 - 1;
-      ChainStage<BITS, MT> st[P];
-#pragma unroll
-      for (int p = 0; p < P; ++p) {
-        load_chain_stage<BITS, MT>(st[p], ra, rbuf, voff_a, voff_b, min(c0 + p, last));
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      stage_to_lds<BITS, MT>(st[0], wlds, wr_off, wrap_off);
-      // chunk i (0-based in the chain) uses VGPR stage i % P and LDS slot i % 2;
-      // the next chunk is copied to LDS before chunk i is decoded.
-      int i = 0;
-      for (; i + P < n; i += P) {
-#pragma unroll
-        for (int p = 0; p < P; ++p) {
-          stage_to_lds<BITS, MT>(st[(p + 1) % P], wlds + ((p + 1) % 2) * SB::kSlot, wr_off, wrap_off);
-          compute_chain_chunk<BITS, MT>(wlds + (p % 2) * SB::kSlot, rd_off, st[p], shift, cbc, acc);
-          load_chain_stage<BITS, MT>(st[p], ra, rbuf, voff_a, voff_b, min(c0 + i + p + P, last));
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
-      // the last 1..P chunks, already loaded
-      const int r = n - i;
-#pragma unroll
-      for (int p = 0; p < P; ++p) {
-        if (p < r) {
-          if (p + 1 < r) stage_to_lds<BITS, MT>(st[(p + 1) % P], wlds + ((p + 1) % 2) * SB::kSlot, wr_off, wrap_off);
-          compute_chain_chunk<BITS, MT>(wlds + (p % 2) * SB::kSlot, rd_off, st[p], shift, cbc, acc);
-        }
-      }
+      // in 128 VGPRs (W = 8) only 2 chunks of more than two 128-bit loads fit
+      constexpr int P = (W == 8 && SB::kLoads > 2) ? 2 : ChainDepth<MT>::P;
+      run_chain<BITS, MT, P>(acc, (int)(((int64_t)s * C) / S), (int)(((int64_t)(s + 1) * C) / S), wlds, x);
     }
     if constexpr (CHAINED) {
       // fold this round's chains into the running sum in split order
-      float *pbuf = (float *)lds;                        // [kWaves][R][128]
+      float *pbuf = (float *)lds;                        // [W][R][128]
       __syncthreads();                                   // every wave is done with its staging
       if (active) {
 #pragma unroll
@@ -675,10 +832,10 @@ __global__ __launch_bounds__(kThreads) void linear_chain_kernel(const LinearArgs
               pbuf[(wave * R + 16 * mt + 4 * g + rr) * kBlockCols + 16 * t + c] = acc[mt][t][rr];
       }
       __syncthreads();
-      const int in_round = min(kWaves, S - round * kWaves);
+      const int in_round = min(W, S - round * W);
 #pragma unroll
-      for (int e = 0; e < R * kBlockCols / kThreads; ++e) {
-        const int idx = threadIdx.x + e * kThreads;
+      for (int e = 0; e < R * kBlockCols / NT; ++e) {
+        const int idx = threadIdx.x + e * NT;
         float v = round == 0 ? pbuf[idx] : zsum[e] + pbuf[idx];
         for (int w = 1; w < in_round; ++w) v = v + pbuf[w * R * kBlockCols + idx];
         zsum[e] = v;
@@ -701,15 +858,12 @@ __global__ __launch_bounds__(kThreads) void linear_chain_kernel(const LinearArgs
     }
   }
 
-  const float sc0 = fp16_to_f32(m.scales[col0 + lane]);
-  const float sc1 = fp16_to_f32(m.scales[col0 + lane + 64]);
-  const float sv0 = fp16_to_f32(m.svh[col0 + lane]);
-  const float sv1 = fp16_to_f32(m.svh[col0 + lane + 64]);
   float *zrow = (float *)(lds + kFoldBytes);             // [R][128]
+  const EpiCols ec = epi_cols(m, col0, lane);
 
   if constexpr (CHAINED) {
 #pragma unroll
-    for (int e = 0; e < R * kBlockCols / kThreads; ++e) zrow[threadIdx.x + e * kThreads] = zsum[e];
+    for (int e = 0; e < R * kBlockCols / NT; ++e) zrow[threadIdx.x + e * NT] = zsum[e];
   } else {
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);             // this wave's partial stores are complete
     __syncthreads();
@@ -722,12 +876,12 @@ __global__ __launch_bounds__(kThreads) void linear_chain_kernel(const LinearArgs
     __syncthreads();
     if (!s_last) return;
     if (threadIdx.x == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    // Sum the S partials in split order. Thread x owns fragments x and
-    // x + 256 (of MT * 512); their loads are issued 8 splits at a time
-    // (clamped to the last split) before they are added.
+    // Sum the S partials in split order. Thread x owns fragments x, x + NT,
+    // ... (of MT * 512); their loads are issued 8 splits at a time (clamped to
+    // the last split) before they are added.
 #pragma unroll
-    for (int e = 0; e < MT * 2; ++e) {
-      const int f = threadIdx.x + e * kThreads;          // fragment index: mt, t, lane
+    for (int e = 0; e < MT * 512 / NT; ++e) {
+      const int f = threadIdx.x + e * NT;                // fragment index: mt, t, lane
       const int fl = f & 63, ft = (f >> 6) & 7, fmt = f >> 9;
       const int fr0 = 16 * fmt + 4 * (fl >> 4);          // first of its 4 rows in the row block
       if (row_base + fr0 < M) {
@@ -750,12 +904,9 @@ __global__ __launch_bounds__(kThreads) void linear_chain_kernel(const LinearArgs
     }
   }
   __syncthreads();
-  for (int rr = wave; rr < R; rr += kWaves) {
-    const int row = row_base + rr;
-    if (row >= M) break;
-    epilogue_row(zrow[rr * kBlockCols + lane], zrow[rr * kBlockCols + lane + 64], lane, sc0, sc1, sv0, sv1,
-                 m.y + (int64_t)row * m.ldy + col0);
-  }
+  // 4 rows per wave and pass
+  for (int r4 = 4 * wave; r4 < R && row_base + r4 < M; r4 += 4 * W)
+    epilogue_rows_lds<1>(zrow + r4 * kBlockCols, kBlockCols, ec, lane, m, col0, row_base + r4, M);
 }
 
 // ------------------------------------------------------------ linear, 128-row tiles
@@ -847,7 +998,7 @@ void linear_tile_kernel(const LinearArgs a) {
   const int col0 = nb * kBlockCols;
 
   constexpr int kStage = 2 * TL::kBuf;
-  constexpr int kEpi = 16 * 132 * 4;
+  constexpr int kEpi = 64 * 132 * 4;
   __shared__ __attribute__((aligned(16))) char lds[kStage > kEpi ? kStage : kEpi];
 
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(m.xr, (uint32_t)((uint64_t)M * K * 2));
@@ -940,11 +1091,8 @@ void linear_tile_kernel(const LinearArgs a) {
     if (p < r)
       step(cb + i + p, lds + (p % 2) * TL::kBuf, lds + ((p + 1) % 2) * TL::kBuf, st[p], st[(p + 1) % P], p + 1 < r);
 
-  const float sc0 = fp16_to_f32(m.scales[col0 + lane]);
-  const float sc1 = fp16_to_f32(m.scales[col0 + lane + 64]);
-  const float sv0 = fp16_to_f32(m.svh[col0 + lane]);
-  const float sv1 = fp16_to_f32(m.svh[col0 + lane + 64]);
-  float *zbuf = (float *)lds;                              // [16][132] per m-tile pass
+  float *zbuf = (float *)lds;                              // [64][132]: 64 rows per epilogue pass
+  const EpiCols ec = epi_cols(m, col0, lane);
 
   if constexpr (!CHAINED) {
     // split sg's partial in the fragment layout, then the counter exchange
@@ -994,25 +1142,24 @@ void linear_tile_kernel(const LinearArgs a) {
       }
   }
 
-  // epilogue, one 16-row m-tile at a time through LDS
+  // epilogue: the 128 rows in two passes of 64 through LDS; in each pass
+  // wave w finishes rows 16w .. 16w + 15 of the pass
 #pragma unroll
-  for (int mtg = 0; mtg < 8; ++mtg) {
-    const int row0 = row_base + 16 * mtg;
-    if (row0 >= M) break;                                  // uniform
+  for (int pass = 0; pass < 2; ++pass) {
+    const int prow = row_base + 64 * pass;
+    if (prow >= M) break;                                  // uniform
     __syncthreads();
-    if (wr == (mtg >> 2)) {
+    if (wr == pass) {
 #pragma unroll
-      for (int i2 = 0; i2 < 4; ++i2)
+      for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) zbuf[(4 * g + q) * 132 + 16 * (4 * wc + i2) + c] = z[mtg & 3][i2][q];
+        for (int i2 = 0; i2 < 4; ++i2)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) zbuf[(16 * mt + 4 * g + q) * 132 + 16 * (4 * wc + i2) + c] = z[mt][i2][q];
     }
     __syncthreads();
-    for (int rr = wave; rr < 16; rr += kWaves) {
-      const int row = row0 + rr;
-      if (row < M)
-        epilogue_row(zbuf[rr * 132 + lane], zbuf[rr * 132 + lane + 64], lane, sc0, sc1, sv0, sv1,
-                     m.y + (int64_t)row * m.ldy + col0);
-    }
+    if (prow + 16 * wave < M)
+      epilogue_rows_lds<4>(zbuf + 16 * wave * 132, 132, ec, lane, m, col0, prow + 16 * wave, M);
   }
 }
 
@@ -1068,35 +1215,36 @@ __global__ void fill_zero_kernel(uint32_t *p, int64_t n) {
 typedef void (*LinearFn)(const LinearArgs);
 
 template <int BITS, bool CHAINED>
-constexpr LinearFn pick_mt(int mti) {
-  return mti == 0 ? linear_chain_kernel<BITS, 1, CHAINED>
-       : mti == 1 ? linear_chain_kernel<BITS, 2, CHAINED>
-       : mti == 2 ? linear_ntile_kernel<BITS, 4, CHAINED>
-                  : linear_tile_kernel<BITS, CHAINED>;
+constexpr LinearFn pick_kernel(int kernel) {
+  return kernel == kChain16   ? linear_chain_kernel<BITS, 1, CHAINED, 4>
+       : kernel == kChain32   ? linear_chain_kernel<BITS, 2, CHAINED, 4>
+       : kernel == kNtile64   ? linear_ntile_kernel<BITS, 4, CHAINED>
+                              : linear_tile_kernel<BITS, CHAINED>;
 }
 
 template <int BITS>
-LinearFn pick_linear(int mti, bool chained) {
-  return chained ? pick_mt<BITS, true>(mti) : pick_mt<BITS, false>(mti);
+LinearFn pick_linear(int kernel, bool chained) {
+  if (kernel == kChain16x8) return linear_chain_kernel<BITS, 1, true, 8>;
+  return chained ? pick_kernel<BITS, true>(kernel) : pick_kernel<BITS, false>(kernel);
 }
 
 }  // namespace
 
-int launch_linear(const LinearArgs &a, int bits, int m_tiles, bool chained, void *stream) {
-  const int mti = m_tiles == 1 ? 0 : m_tiles == 2 ? 1 : m_tiles == 4 ? 2 : 3;
+int launch_linear(const LinearArgs &a, int bits, int kernel, bool chained, void *stream) {
+  if (kernel < kChain16 || kernel > kTile128 || (kernel == kChain16x8 && !chained)) return (int)hipErrorInvalidValue;
   LinearFn fn = nullptr;
   switch (bits) {
-    case 2: fn = pick_linear<2>(mti, chained); break;
-    case 3: fn = pick_linear<3>(mti, chained); break;
-    case 4: fn = pick_linear<4>(mti, chained); break;
-    case 5: fn = pick_linear<5>(mti, chained); break;
-    case 6: fn = pick_linear<6>(mti, chained); break;
-    case 7: fn = pick_linear<7>(mti, chained); break;
-    case 8: fn = pick_linear<8>(mti, chained); break;
+    case 2: fn = pick_linear<2>(kernel, chained); break;
+    case 3: fn = pick_linear<3>(kernel, chained); break;
+    case 4: fn = pick_linear<4>(kernel, chained); break;
+    case 5: fn = pick_linear<5>(kernel, chained); break;
+    case 6: fn = pick_linear<6>(kernel, chained); break;
+    case 7: fn = pick_linear<7>(kernel, chained); break;
+    case 8: fn = pick_linear<8>(kernel, chained); break;
     default: return (int)hipErrorInvalidValue;
   }
   (void)hipGetLastError();   // report this launch's error, not an earlier one
-  hipLaunchKernelGGL(fn, dim3((unsigned)a.total_wgs), dim3(kThreads), 0, (hipStream_t)stream, a);
+  hipLaunchKernelGGL(fn, dim3((unsigned)a.total_wgs), dim3(threads_per_wg(kernel)), 0, (hipStream_t)stream, a);
   return (int)hipGetLastError();
 }
 
