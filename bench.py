@@ -163,7 +163,7 @@ def main():
                     help="also run one plain 1 GiB device copy (PMC scale reference)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for {args.gpus}).",
+        print(f"bench.py measures one GPU only: the library has no multi-GPU path (asked for {args.gpus}).",
               file=sys.stderr)
         sys.exit(2)
 
@@ -231,7 +231,7 @@ def main():
     log(f"gate/up linear: {ms_kernel * 1e3:.2f} us per launch -> {achieved:.1f} GB/s")
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_record(),
-                "kernel": "linear_kernel<bits=4, m_tiles=1> of the {gate, up} group, M=16",
+                "kernel": "linear_chain_kernel<4, 1, true, 8> (the {gate, up} group, M=16)",
                 "alg_bytes_per_launch": kbytes, "us_per_launch": round(ms_kernel * 1e3, 3)}
 
     extra = {}

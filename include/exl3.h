@@ -101,8 +101,8 @@ typedef struct exl3_workspace {
 /* exl3_plan — the K-split plan of a K x N weight at `bits` bits.
  * It depends on (K, N, bits) only, never on the row count, and every N of at
  * least EXL3_WIDE_BLOCKS blocks plans alike, so a column view that wide plans
- * as its whole parent does (TensorFold PR #1507, review and follow-up: "any
- * view of 64 blocks or more plans like the full head"; wide_blocks = 64).
+ * as its whole parent does (TensorFold PR #1507, review and follow-up: a view
+ * of at least 64 blocks takes the full head's plan; wide_blocks = 64).
  * Errors: EINVAL (out == NULL), EALIGN (K or N not a multiple of 128 or
  * zero), EBITS. */
 #define EXL3_WIDE_BLOCKS 64

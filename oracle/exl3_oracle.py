@@ -30,13 +30,12 @@ print neither the codebook nor the bit layout.  What they do fix, and where:
   * decoded weights are fp16 and K sums are fp32; a constant weight times
     rotated inputs of 4096 overflows fp16 sums but not fp32 ones
     (PR #1467, author follow-up on the kernel contract, gate 4);
-  * code windows start at odd offsets at odd widths, so a 0xaaaa fill decodes
-    to two alternating weights at 3 and 5 bits, while all-ones states with
-    scales of 1 decode to one weight at every width (PR #1467, author
-    follow-up "Gate 4" after the width-matrix review);
+  * at odd widths the code windows begin at odd bit offsets, so a 0xaaaa
+    fill decodes to two alternating weights at 3 and 5 bits, while all-ones
+    states with unit scales decode to one weight at every width (PR #1467,
+    author follow-up, gate 4, after the width-matrix review);
   * per-column scales and a per-member input sign vector suh (PR #1467, gates
-    and planted controls: "a group with one member's scales swapped",
-    "rot_group with one member's suh swapped");
+    and planted controls that swap one group member's scales or its suh);
   * column views are whole 128-column blocks that keep the parent's strides
     (PR #1507, "What this changes");
   * planted NaN and both infinities reach the outputs (PR #1467, gate 1).

@@ -88,7 +88,7 @@ def gpu_blocks(y_dev, blocks, rows=None):
 
 
 def assert_close(got_bits, ref_bits, rel=1e-2, what=""):
-    """Y within rel * max|Y_oracle| element by element (the spec bar),
+    """Y within rel * max|Y_oracle| element by element (the parity bar),
     with NaN positions identical and infinities identical."""
     g = O.bf16_to_f64(got_bits)
     r = O.bf16_to_f64(ref_bits)

@@ -220,9 +220,9 @@ def check_view_decode_equals_parent_columns():
 
 
 def check_head_byte_accounting():
-    """TensorFold PR #1507: the 6-bit head 5120 -> 248,320 skips "~545 MB" when
-    only the two span views are read, and a 64-block tail reads "about 30 MB
-    more" than a 384-column (3-block) tail; the first span is 39.7 % of the
+    """TensorFold PR #1507: the 6-bit head 5120 -> 248,320 skips roughly 545 MB
+    when only the two span views are read, and a 64-block tail reads roughly
+    30 MB more than a 384-column (3-block) tail; the first span is 39.7 % of the
     vocabulary with the 288 kept tail columns.  Storage is exactly 6 bits per
     weight, so a block is 5120*128*6/8 bytes."""
     K, bits = 5120, 6

@@ -2,7 +2,7 @@
 
 Bit-exact: the codebook on all 65,536 states, decoded weights at every width
 (2..8 bits), the pages' fill patterns, and closed-form outputs whose every
-intermediate is exact. Within the benchmark spec's tolerance (max |Y - Y_oracle| <=
+intermediate is exact. Within the parity tolerance (max |Y - Y_oracle| <=
 1e-2 max |Y_oracle|, NaN/Inf positions identical): the linear on the five
 configurations of the 27B layer, at full size on sampled column blocks and
 rows where the oracle cannot do the whole output in seconds.
