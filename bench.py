@@ -231,7 +231,7 @@ def main():
     log(f"gate/up linear: {ms_kernel * 1e3:.2f} us per launch -> {achieved:.1f} GB/s")
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_record(),
-                "kernel": "linear_chain_kernel<4, 1, true, 8> (the {gate, up} group, M=16)",
+                "kernel": "linear_spread_kernel<4> (the {gate, up} group, M=16)",
                 "alg_bytes_per_launch": kbytes, "us_per_launch": round(ms_kernel * 1e3, 3)}
 
     extra = {}

@@ -202,7 +202,10 @@ int exl3_test_rot_in(const exl3_weight_t *w, const void *x, int64_t ldx, int64_t
  * the bits of a row:
  *   m_tiles: -1 automatic, else 1, 2, 4 or 8 16-row MFMA tiles per workgroup;
  *   chained: -1 automatic, 0 one K split per workgroup with counter exchange,
- *            1 every split of a block in one workgroup, summed in order.
+ *            1 every split of a block in one workgroup, summed in order,
+ *            2 the spread launch (up to 16 rows, one S <= 15 for every
+ *            member; otherwise as 1): a 16-wave workgroup per owned block,
+ *            its spare waves taking splits of the remaining blocks.
  * `splits` (0 = the plan's) overrides S and DOES change bits: it is the
  * planted control "another K split". */
 int exl3_test_force(int32_t m_tiles, int32_t chained, int32_t splits);

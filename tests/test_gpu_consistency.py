@@ -1,8 +1,8 @@
 """GPU self-consistency, bitwise: a row's bytes do not depend on how many rows
 are in the call, on the row tiling or launch shape, on group membership or on
 column views (TensorFold PR #1467 "The arithmetic" and its gate 3; PR #1407
-review item 1; PR #1507 "the views plan as the whole head, so the logits keep
-their bits"). Counters are zero whenever no call runs (PR #1475).
+review item 1; PR #1507 review: views plan as the whole head does, so the
+logits keep their bits). Counters are zero whenever no call runs (PR #1475).
 
 Planted controls (another K split, a member's scales swapped, a member's suh
 swapped) must change bytes, which shows the comparisons can see a change.
@@ -31,7 +31,7 @@ def _hooks():
     ex().exl3_test_force(-1, -1, 0)
 
 
-# weights covering each plan kind: narrow (S=32 and S=8), wide (S=4), K=17408
+# weights covering each plan kind: narrow (S = 16), wide (S = 15), K = 17408, 3 and 6 bits
 SHAPES = [("k", 5120, 1024, 4), ("q", 5120, 6144, 4), ("wide", 5120, 8192, 4), ("down", 17408, 5120, 4),
           ("gate3", 5120, 2048, 3), ("head6", 5120, 8192, 6)]
 
@@ -52,19 +52,52 @@ def test_rows_identical_for_every_row_count(name, K, N, bits):
 def test_rows_identical_for_every_tiling_and_launch_shape(name, K, N, bits):
     """The min_rows analogue: force each row tiling (1, 2, 4, 8 MFMA row tiles
     per workgroup) and each launch shape (one split per workgroup with counter
-    exchange, or every split in one workgroup) at several row counts."""
+    exchange, every split in one workgroup, and at 16 rows the spread launch)
+    at several row counts."""
     L = G.layer("tiling", name, K, N, bits)
     w = G.upload(L)
     x = G.xbits("tiling", 40, K)
     xd = G.dev_bf16(x)
     ref = G.host_u16(G.run(w, xd, M=40, tag="auto"))
     for mt in (1, 2, 4, 8):
-        for chained in (0, 1):
+        for chained in ((0, 1, 2) if mt == 1 else (0, 1)):
             ex().exl3_test_force(mt, chained, 0)
             for M in (1, 16, 17, 40):
                 y = G.host_u16(G.run(w, xd, M=M, tag=f"forced m_tiles={mt} chained={chained}"))
                 assert np.array_equal(y[:M], ref[:M]), (name, mt, chained, M)
     ex().exl3_test_force(-1, -1, 0)
+
+
+@pytest.mark.parametrize("M", [1, 16])
+def test_spread_launch_with_many_left_blocks(M):
+    """The spread launch with 4 splits per block: 12 spare waves per workgroup,
+    three quarters of the blocks finished by spare waves, several per
+    workgroup; bitwise equal to the chained and the exchanged launch of the
+    same plan."""
+    L = G.layer("spread", "q", synth.HIDDEN, synth.Q_COLS, 4)
+    w = G.upload(L)
+    xd = G.dev_bf16(G.xbits("spread", M, synth.HIDDEN))
+    out = {}
+    for chained in (2, 1, 0):
+        ex().exl3_test_force(1, chained, 4)
+        out[chained] = G.host_u16(G.run(w, xd, tag=f"splits=4 chained={chained}"))
+    ex().exl3_test_force(-1, -1, 0)
+    assert np.array_equal(out[2], out[1]) and np.array_equal(out[2], out[0])
+
+
+def test_gate_up_group_spread_equals_other_launches():
+    """The {gate, up} group at 16 rows (272 blocks at S = 15: one block per CU
+    and the 16 left blocks on spare waves) against the chained and the
+    exchanged launch."""
+    K = synth.HIDDEN
+    ws_ = [G.upload(G.layer("spread-gu", n, K, synth.INTERMEDIATE, 4)) for n in ("gate", "up")]
+    xd = G.dev_bf16(G.xbits("spread-gu", 16, K))
+    auto = [G.host_u16(y) for y in G.run_group(ws_, xd, tag="gate+up auto")]
+    for chained in (1, 0):
+        ex().exl3_test_force(1, chained, 0)
+        other = [G.host_u16(y) for y in G.run_group(ws_, xd, tag=f"gate+up chained={chained}")]
+        ex().exl3_test_force(-1, -1, 0)
+        assert all(np.array_equal(a, b) for a, b in zip(auto, other)), chained
 
 
 def test_prompt_rows_equal_decode_rows():
@@ -138,7 +171,8 @@ def test_another_k_split_changes_bits():
 def test_views_equal_full_head_columns():
     """PR #1507: span views of >= 64 blocks plan as the whole head, so their
     output is the head's output byte for byte; a 3-block view plans otherwise
-    and is the control that goes red. Full 6-bit head 5120 -> 248,320, M = 16."""
+    and is the control that goes red (against span B, over 128 rows). Full
+    6-bit head 5120 -> 248,320, M = 16."""
     K, N, M = 5120, synth.VOCAB, 16
     L = G.layer("views", "head", K, N, 6)
     w = G.upload(L)
@@ -150,9 +184,13 @@ def test_views_equal_full_head_columns():
     assert np.array_equal(b, full[:, 240128:])
     kept = b[:, 248032 - 240128:]
     assert kept.shape[1] == 288 and np.array_equal(kept, full[:, 248032:])
-    tail3 = G.host_u16(G.run(w.columns(248320 - 384, 384), xd, tag="3-block tail"))
+    # control: the 3-block tail plans otherwise; over 128 rows (49,152
+    # outputs) some bf16 output moves with the summation order
     assert ex().exl3_plan(K, 384, 6).splits != ex().exl3_plan(K, N, 6).splits
-    assert not np.array_equal(tail3, full[:, -384:])
+    x128 = G.dev_bf16(G.xbits("views", 128, K))
+    b128 = G.host_u16(G.run(w.columns(240128, 8192), x128, tag="span B, 128 rows"))
+    tail3 = G.host_u16(G.run(w.columns(248320 - 384, 384), x128, tag="3-block tail, 128 rows"))
+    assert not np.array_equal(tail3, b128[:, -384:])
 
 
 def test_counters_zero_at_rest_and_repeats_identical():

@@ -77,16 +77,19 @@ def test_plan_every_wide_n_equal(lib):
 def test_plan_table_fills_the_gpu(lib):
     """Narrow weights split until about two splits per SIMD (n_blocks * S >=
     512), at most 16 ways, keeping >= 4 chunks per split; wide ones take
-    S_wide(K) <= 8 with >= 16 chunks per split."""
+    S_wide(K) = 15 (15 chains and a spare wave per 16-wave workgroup) unless
+    that leaves fewer than 4 chunks per split."""
     for K, N in ((5120, 1024), (5120, 6144), (17408, 5120), (256, 256), (1024, 384)):
         p = ex.exl3_plan(K, N, 4)
         assert p.n_blocks < 64
         assert p.n_blocks * p.splits >= 512 or p.splits == 16 or p.chunks // (2 * p.splits) < 4
         assert p.chunks // p.splits >= 4 or p.splits == 1
-    for K in (1024, 5120, 17408):
+    for K, want in ((128, 1), (1024, 8), (1920, 15), (5120, 15), (17408, 15)):
         p = ex.exl3_plan(K, 64 * 128, 4)
-        assert p.splits <= 8 and (p.chunks // p.splits >= 16 or p.splits == 1)
-    assert ex.exl3_plan(5120, 248320, 6).splits == 8
+        assert p.splits == want, (K, p.splits)
+        assert p.chunks // p.splits >= 4 or p.splits == 1
+    assert ex.exl3_plan(5120, 248320, 6).splits == 15
+    assert ex.exl3_plan(5120, 17408, 4).splits == 15
     assert ex.exl3_plan(5120, 1024, 4).splits == 16
 
 
@@ -285,7 +288,7 @@ def test_strerror_covers_every_code(lib):
 
 def test_test_force_validation(lib):
     assert lib.exl3_test_force(3, -1, 0) == ex.EXL3_EINVAL
-    assert lib.exl3_test_force(-1, 2, 0) == ex.EXL3_EINVAL
+    assert lib.exl3_test_force(-1, 3, 0) == ex.EXL3_EINVAL
     assert lib.exl3_test_force(-1, -1, -1) == ex.EXL3_EINVAL
     assert lib.exl3_test_force(8, 1, 4) == ex.EXL3_OK
 

@@ -55,23 +55,21 @@ int check_weight(const exl3_weight_t *w) {
 
 // The plan table. S depends on (K, N, bits) only, measured on MI355X at 1
 // and 16 rows (one K split per wave, 256 CUs):
-//  * a weight of at least EXL3_WIDE_BLOCKS blocks takes S_wide(K): the
-//    largest power of two up to 8 that keeps 16 chunks (512 K) per split, so
-//    every such view plans alike. At K = 5120 that is 8: the 64-block tail of
-//    the head then gets 512 waves, and the whole head keeps 20 chunks per
-//    wave;
+//  * a weight of at least EXL3_WIDE_BLOCKS blocks takes S_wide(K) = 15 when
+//    that keeps at least 4 chunks (128 K) per split, else as many splits as
+//    keep 4 chunks each; every such view plans alike. 15 chains fill 15 of a
+//    16-wave workgroup, and the 16th wave of every workgroup takes a split of
+//    the blocks that exceed one block per CU (the spread launch): a group of
+//    272 blocks on 256 CUs then runs 16 waves on every CU;
 //  * a narrower weight takes the smallest power of two with n_blocks * S >=
 //    512 (about two splits per SIMD), at most 16 and keeping at least 4
-//    chunks (128 K) per split.
+//    chunks per split.
 int32_t splits_for(int64_t K, int64_t N, int32_t bits) {
   (void)bits;
   const int64_t chunks = K / kChunk;
   const int64_t nb = N / kBlockCols;
   int32_t s = 1;
-  if (nb >= EXL3_WIDE_BLOCKS) {
-    while (s < 8 && chunks / (2 * s) >= 16) s *= 2;
-    return s;
-  }
+  if (nb >= EXL3_WIDE_BLOCKS) return (int32_t)std::max<int64_t>(1, std::min<int64_t>(15, chunks / 4));
   while (nb * s < 512 && s < 16 && chunks / (2 * s) >= 4) s *= 2;
   return s;
 }
@@ -85,14 +83,30 @@ struct MemberPlan {
 struct Launch {
   int m_tiles;
   int kernel;               // exl3::LinearKernel
-  bool chained;
+  bool chained;             // no exchange between workgroups (the spread launch exchanges left blocks only)
+  bool exchange;            // partials and counters in the workspace
   int64_t row_blocks;
+  int64_t own_blocks = 0;   // spread launch
+  int64_t left_blocks = 0;  // spread launch
 };
 
+// CUs of the current device (256 on MI355X; 256 when no device answers).
+int cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
 // Decode rows (up to 16): at or above this many blocks, one 8-wave workgroup
-// per block (chained splits, two workgroups per CU) keeps every CU busy
-// without partials; below it, K splits exchange partials across workgroups.
-constexpr int64_t kChainedMinBlocks16 = 256;
+// per block (chained splits, two workgroups per CU) keeps every CU busy for
+// several rounds without partials.
+constexpr int64_t kChainedMinBlocks16 = 512;
 
 Launch choose_launch(const MemberPlan *mp, int n, int64_t M) {
   Launch L;
@@ -106,10 +120,39 @@ Launch choose_launch(const MemberPlan *mp, int n, int64_t M) {
     all_single = all_single && mp[j].splits == 1;
     blocks += mp[j].n_blocks;
   }
-  if (g_hooks.chained == 0 || g_hooks.chained == 1) {
-    L.chained = g_hooks.chained == 1;
+  // one plan S <= 15 for every member and one 16-row block: the spread
+  // launch is possible
+  int32_t s_uniform = mp[0].splits;
+  for (int j = 1; j < n; ++j)
+    if (mp[j].splits != s_uniform) s_uniform = 0;
+  if (s_uniform > 15) s_uniform = 0;
+  const int64_t ncu = cu_count();
+  L.exchange = false;
+  bool spread = false;
+  if (g_hooks.chained >= 0 && g_hooks.chained <= 2) {
+    L.chained = g_hooks.chained != 0;
+    if (g_hooks.chained == 2 && mt == 1 && L.row_blocks == 1 && s_uniform > 0) {
+      // forced: as many left blocks as the spare waves can take
+      spread = true;
+      L.left_blocks = blocks * (16 - s_uniform) / 16;
+      L.own_blocks = blocks - L.left_blocks;
+    }
   } else if (mt == 1) {
-    L.chained = all_single || blocks >= kChainedMinBlocks16;
+    if (all_single || blocks >= kChainedMinBlocks16) {
+      L.chained = true;
+    } else if (L.row_blocks > 1 || s_uniform == 0) {
+      L.chained = false;
+    } else if (blocks > ncu && (blocks - ncu) * s_uniform <= ncu * (16 - s_uniform)) {
+      L.chained = spread = true;
+      L.own_blocks = ncu;
+      L.left_blocks = blocks - ncu;
+    } else if (4 * blocks >= 3 * ncu && blocks <= ncu) {
+      L.chained = spread = true;
+      L.own_blocks = blocks;
+      L.left_blocks = 0;
+    } else {
+      L.chained = false;
+    }
   } else {
     // Partials and counters only when the grid would otherwise be too small
     // to stream HBM: an exchange costs a few microseconds of serialized
@@ -118,10 +161,12 @@ Launch choose_launch(const MemberPlan *mp, int n, int64_t M) {
     // blocks and wide weights give enough workgroups by themselves.
     L.chained = all_single || M > 128 || L.row_blocks * blocks >= 256;
   }
-  L.kernel = mt == 1 ? (L.chained ? exl3::kChain16x8 : exl3::kChain16)
+  L.kernel = spread    ? exl3::kSpread16
+           : mt == 1 ? (L.chained ? exl3::kChain16x8 : exl3::kChain16)
            : mt == 2 ? exl3::kChain32
            : mt == 4 ? exl3::kNtile64
                      : exl3::kTile128;
+  L.exchange = !L.chained || (spread && L.left_blocks > 0);
   return L;
 }
 
@@ -136,7 +181,7 @@ Layout layout_for(const MemberPlan *mp, int n, int64_t M, int64_t K, const Launc
   Layout lay{};
   for (int j = 0; j < n; ++j) {
     lay.xr_bytes[j] = align_up((size_t)M * K * 2);
-    if (!L.chained) {
+    if (L.exchange) {
       // rows padded to whole row blocks (the fragment layout of the 16- and
       // 32-row tilings stores whole 16-row tiles)
       lay.part_bytes[j] = align_up((size_t)mp[j].splits * (L.row_blocks * 16 * L.m_tiles) * mp[j].w->N * 4);
@@ -288,6 +333,7 @@ int run_group(int32_t n_members, const exl3_weight_t *const *w, const void *x, i
   size_t off = ws->counter_bytes;
   size_t counter_off = 0;
   int64_t wg = 0;
+  int64_t blocks_before = 0;
   for (int j = 0; j < n_members; ++j) {
     const exl3_weight_t *wj = w[j];
     uint16_t *xr = (uint16_t *)(base + off);
@@ -306,8 +352,9 @@ int run_group(int32_t n_members, const exl3_weight_t *const *w, const void *x, i
     m.n_blocks = mp[j].n_blocks;
     m.splits = mp[j].splits;
     m.groups = exl3::groups_per_block(mp[j].splits, L.kernel, L.chained);
-    m.wg_begin = (int32_t)wg;
-    if (!L.chained) {
+    m.wg_begin = (int32_t)(L.kernel == exl3::kSpread16 ? blocks_before : wg);
+    blocks_before += mp[j].n_blocks;
+    if (L.exchange) {
       m.partials = (float *)(base + off);
       off += lay.part_bytes[j];
       m.counters = (uint32_t *)base + counter_off;
@@ -315,7 +362,10 @@ int run_group(int32_t n_members, const exl3_weight_t *const *w, const void *x, i
     }
     wg += L.row_blocks * mp[j].n_blocks * m.groups;
   }
+  if (L.kernel == exl3::kSpread16) wg = L.own_blocks;
   if (wg >= (int64_t(1) << 31)) return EXL3_EINVAL;
+  la.own_blocks = (int32_t)L.own_blocks;
+  la.left_blocks = (int32_t)L.left_blocks;
   ra.x = (const uint16_t *)x;
   ra.ldx = ldx;
   ra.M = (int32_t)M;
@@ -435,7 +485,7 @@ int exl3_test_rot_in(const exl3_weight_t *w, const void *x, int64_t ldx, int64_t
 
 int exl3_test_force(int32_t m_tiles, int32_t chained, int32_t splits) {
   if (!(m_tiles == -1 || m_tiles == 1 || m_tiles == 2 || m_tiles == 4 || m_tiles == 8)) return EXL3_EINVAL;
-  if (chained < -1 || chained > 1 || splits < 0) return EXL3_EINVAL;
+  if (chained < -1 || chained > 2 || splits < 0) return EXL3_EINVAL;
   g_hooks.m_tiles = m_tiles;
   g_hooks.chained = chained;
   g_hooks.splits = splits;

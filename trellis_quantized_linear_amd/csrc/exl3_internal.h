@@ -28,7 +28,8 @@ struct MemberArgs {
   int32_t n_blocks;
   int32_t splits;             // S of the plan
   int32_t groups;             // workgroups per (row block, column block); 1 when chained
-  int32_t wg_begin;           // first workgroup of this member in the grid
+  int32_t wg_begin;           // first workgroup of this member in the grid (spread launch:
+                              // the member's first block among the launch's blocks)
 };
 
 struct LinearArgs {
@@ -39,6 +40,8 @@ struct LinearArgs {
   int32_t chunks;             // K / 32
   int32_t row_blocks;         // ceil(M / (16 * m_tiles))
   int32_t total_wgs;
+  int32_t own_blocks;         // spread launch: blocks owned by one workgroup each (= total_wgs)
+  int32_t left_blocks;        // spread launch: blocks whose splits go to spare waves
 };
 
 struct RotArgs {
@@ -67,9 +70,10 @@ enum LinearKernel {
   kChain32 = 2,     // 32 rows, 4 waves per workgroup, one split per wave
   kNtile64 = 3,     // 64 rows per workgroup, waves own column tiles
   kTile128 = 4,     // 128 rows per workgroup, 2 x 2 waves of 64 x 64
+  kSpread16 = 5,    // 16 rows, 16 waves: one own block per workgroup + spare waves on left blocks
 };
 
-inline int waves_per_wg(int kernel) { return kernel == kChain16x8 ? 8 : kWaves; }
+inline int waves_per_wg(int kernel) { return kernel == kSpread16 ? 16 : kernel == kChain16x8 ? 8 : kWaves; }
 inline int threads_per_wg(int kernel) { return 64 * waves_per_wg(kernel); }
 
 // Arrivals per (row block, column block) of a launch: one when every split of

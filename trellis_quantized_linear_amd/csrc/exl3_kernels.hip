@@ -652,17 +652,26 @@ __device__ __forceinline__ void stage_to_lds(const ChainStage<BITS, MT> &st, cha
   }
 }
 
-template <int BITS, int MT>
-__device__ __forceinline__ void compute_chain_chunk(const char *slot, uint32_t rd_off, const ChainStage<BITS, MT> &st,
-                                                    uint32_t shift, const CbConst &cb, f32x4 (&acc)[MT][8]) {
-  constexpr int ND = BitsTraits<BITS>::kDwords;
+// The lane's words of a staged chunk: 2 or 3 dwords of each of the 8 tiles.
+// All 8 reads are issued together so that their LDS latencies overlap.
+template <int BITS>
+__device__ __forceinline__ void read_chain_chunk(const char *slot, uint32_t rd_off,
+                                                 uint32_t (&w)[8][BitsTraits<BITS>::kDwords]) {
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
     const uint32_t *q = (const uint32_t *)(slot + rd_off + t * Stream<BITS>::kStride);
-    uint32_t w[ND];
 #pragma unroll
-    for (int d = 0; d < ND; ++d) w[d] = q[d];
-    const half8 bf = decode8<BITS>(w, shift, cb);
+    for (int d = 0; d < BitsTraits<BITS>::kDwords; ++d) w[t][d] = q[d];
+  }
+}
+
+template <int BITS, int MT>
+__device__ __forceinline__ void decode_chain_chunk(const uint32_t (&w)[8][BitsTraits<BITS>::kDwords],
+                                                   const ChainStage<BITS, MT> &st, uint32_t shift, const CbConst &cb,
+                                                   f32x4 (&acc)[MT][8]) {
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const half8 bf = decode8<BITS>(w[t], shift, cb);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
       acc[mt][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, st.a[mt]), bf, acc[mt][t], 0, 0, 0);
@@ -741,12 +750,17 @@ __device__ __forceinline__ void run_chain(f32x4 (&acc)[MT][8], int c0, int c1, c
     __builtin_amdgcn_sched_barrier(0);
   }
   stage_to_lds<BITS, MT>(st[0], wlds, x.wr_off, x.wrap_off);
+  // per chunk: read the staged chunk's words, stage the next chunk into the
+  // other slot, decode and multiply, refill the register stage
+  uint32_t w[8][BitsTraits<BITS>::kDwords];
   int i = 0;
   for (; i + P < n; i += P) {
 #pragma unroll
     for (int p = 0; p < P; ++p) {
+      read_chain_chunk<BITS>(wlds + (p % 2) * SB::kSlot, x.rd_off, w);
+      __builtin_amdgcn_sched_barrier(0);
       stage_to_lds<BITS, MT>(st[(p + 1) % P], wlds + ((p + 1) % 2) * SB::kSlot, x.wr_off, x.wrap_off);
-      compute_chain_chunk<BITS, MT>(wlds + (p % 2) * SB::kSlot, x.rd_off, st[p], x.shift, x.cb, acc);
+      decode_chain_chunk<BITS, MT>(w, st[p], x.shift, x.cb, acc);
       load_chain_stage<BITS, MT>(st[p], x.ra, x.rb, x.voff_a, x.voff_b, min(c0 + i + p + P, last));
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -756,8 +770,174 @@ __device__ __forceinline__ void run_chain(f32x4 (&acc)[MT][8], int c0, int c1, c
 #pragma unroll
   for (int p = 0; p < P; ++p) {
     if (p < r) {
+      read_chain_chunk<BITS>(wlds + (p % 2) * SB::kSlot, x.rd_off, w);
       if (p + 1 < r) stage_to_lds<BITS, MT>(st[(p + 1) % P], wlds + ((p + 1) % 2) * SB::kSlot, x.wr_off, x.wrap_off);
-      compute_chain_chunk<BITS, MT>(wlds + (p % 2) * SB::kSlot, x.rd_off, st[p], x.shift, x.cb, acc);
+      decode_chain_chunk<BITS, MT>(w, st[p], x.shift, x.cb, acc);
+    }
+  }
+}
+
+// ------------------------------------------------------------ linear, decode rows: spread launch
+//
+// Up to 16 rows, every member planned with the same S <= 15, one 16-wave
+// workgroup per CU. Workgroup u owns launch block u (u < own_blocks): its
+// waves 16-S .. 15 run the block's S chains and the workgroup folds them in
+// split order in LDS, as a chained launch does. Its first 16 - S waves (the
+// oldest, so the first to issue) are spare waves that share the splits of
+// the launch blocks past own_blocks (the "left" blocks): spare wave k of
+// workgroup u takes unit u*(16-S) + k, that is split unit % S of left block
+// unit / S. Those splits meet through the workspace (partials and a counter,
+// as in the exchanged launch); the workgroup whose spare wave arrives last
+// adds them in split order while it folds its own block, and runs that
+// block's epilogue as well. A launch of 272 blocks at S = 15 on 256 CUs thus
+// gives every CU one block plus one split of the 16 left blocks: 16 busy
+// waves, 4 per SIMD, the same work everywhere.
+
+template <int BITS>
+__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4)))
+void linear_spread_kernel(const LinearArgs a) {
+  using SB = Stream<BITS>;
+  constexpr int W = 16, NT = 64 * W;
+  // 4 chunks in flight where a chunk is at most two 128-bit loads per lane,
+  // 2 above that: 128 VGPRs per wave
+  constexpr int P = SB::kLoads <= 2 ? 4 : 2;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int u = blockIdx.x;
+  const int S = a.m[0].splits;                           // the same for every member
+  const int spare = W - S;                               // waves 0 .. spare-1
+  const int M = a.M, K = a.K, C = a.chunks;
+  const int c = lane & 15, g = lane >> 4;
+
+  // LDS: per-wave staging during the chains; afterwards the fold buffers
+  // [S][16][128] and the two 16-row results (own block, left block)
+  constexpr int kTile = 16 * kBlockCols * 4;
+  constexpr int kFold = (W - 1) * kTile;
+  constexpr int kStage = W * SB::kWave;
+  constexpr int kLds = kStage > kFold + 2 * kTile ? kStage : kFold + 2 * kTile;
+  __shared__ __attribute__((aligned(16))) char lds[kLds];
+  __shared__ int s_left[W];                              // left blocks this workgroup finishes
+  __shared__ int s_nleft;
+  char *wlds = lds + wave * SB::kWave;
+  if (threadIdx.x == 0) s_nleft = 0;
+  __syncthreads();
+
+  // member j and block nb of launch block gb (members' blocks are consecutive)
+  auto locate = [&](int gb, int &jj, int &nb) {
+    jj = 0;
+    if (a.n_members > 1 && gb >= a.m[1].wg_begin) jj = 1;
+    if (a.n_members > 2 && gb >= a.m[2].wg_begin) jj = 2;
+    nb = gb - a.m[jj].wg_begin;
+  };
+
+  int jo, nbo;
+  locate(u, jo, nbo);
+  const MemberArgs &mo = a.m[jo];
+  f32x4 acc[1][8];
+  if (wave >= spare) {
+    const int sp = wave - spare;
+    const ChainCtx<BITS, 1> x = chain_ctx<BITS, 1>(mo, M, K, nbo, 0, lane);
+    run_chain<BITS, 1, P>(acc, (int)(((int64_t)sp * C) / S), (int)(((int64_t)(sp + 1) * C) / S), wlds, x);
+  } else {
+    const int unit = u * spare + wave;
+    if (unit < a.left_blocks * S) {
+      const int gb = a.own_blocks + unit / S;
+      const int sp = unit - (unit / S) * S;
+      int jl, nbl;
+      locate(gb, jl, nbl);
+      const MemberArgs &ml = a.m[jl];
+      const ChainCtx<BITS, 1> x = chain_ctx<BITS, 1>(ml, M, K, nbl, 0, lane);
+      run_chain<BITS, 1, P>(acc, (int)(((int64_t)sp * C) / S), (int)(((int64_t)(sp + 1) * C) / S), wlds, x);
+      // the split's partial, agent scope, then the arrival (see the exchanged launch)
+      const __amdgpu_buffer_rsrc_t rp = make_rsrc(partial_frag(ml, sp, 0, nbl, 1, 1), 8 * 1024);
+      if (4 * g < M) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[0][t]), rp, t * 1024 + 16 * lane, 0,
+                                                 kAgentScope);
+      }
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+      uint32_t *counter = ml.counters + nbl;
+      uint32_t prev = 0;
+      if (lane == 0) prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      prev = __builtin_amdgcn_readfirstlane(prev);
+      if (prev == (uint32_t)(S - 1) && lane == 0) {
+        __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_left[atomicAdd(&s_nleft, 1)] = gb;             // at most one per spare wave
+      }
+    }
+  }
+  const EpiCols eco = epi_cols(mo, nbo * kBlockCols, lane);
+  __syncthreads();                                       // staging is free; the left list is final
+
+  float *pbuf = (float *)lds;                            // [S][16][128]
+  float *zown = (float *)(lds + kFold);                  // [16][128]
+  float *zleft = (float *)(lds + kFold + kTile);         // [16][128]
+  if (wave >= spare) {
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr)
+        pbuf[((wave - spare) * 16 + 4 * g + rr) * kBlockCols + 16 * t + c] = acc[0][t][rr];
+  }
+  const int nleft = s_nleft;
+  __syncthreads();
+  // Waves 0..7 fold the own block (P_0 + P_1 + ... in split order, 4 of its
+  // 2048 values per thread); waves 8..15 meanwhile add up the first left
+  // block's S partials in split order (fragment f = thread - 512: column
+  // tile f / 64, lane f % 64), all S loads in flight. Later left blocks (only
+  // when S is small) follow one at a time.
+  auto left_sum = [&](int i, int f) {
+    int jl, nbl;
+    locate(s_left[i], jl, nbl);
+    const MemberArgs &ml = a.m[jl];
+    const int fl = f & 63, ft = f >> 6;
+    const int fr0 = 4 * (fl >> 4);
+    if (fr0 < M) {
+      u32x4 v[15];
+#pragma unroll
+      for (int q = 0; q < 15; ++q) {
+        const __amdgpu_buffer_rsrc_t rq = make_rsrc(partial_frag(ml, min(q, S - 1), 0, nbl, 1, 1), 8 * 1024);
+        v[q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, 16 * f, 0, kAgentScope));
+      }
+      f32x4 zv = __builtin_bit_cast(f32x4, v[0]);
+#pragma unroll
+      for (int q = 1; q < 15; ++q)
+        if (q < S) zv = zv + __builtin_bit_cast(f32x4, v[q]);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) zleft[(fr0 + q) * kBlockCols + 16 * ft + (fl & 15)] = zv[q];
+    }
+  };
+  if (wave < 8) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int idx = threadIdx.x + e * 512;
+      float v = pbuf[idx];
+      for (int sp = 1; sp < S; ++sp) v = v + pbuf[sp * 2048 + idx];
+      zown[idx] = v;
+    }
+  } else if (nleft > 0) {
+    left_sum(0, threadIdx.x - 512);
+  }
+  __syncthreads();
+  // epilogues, 4 rows per wave: waves 0..3 the own block, 4..7 the left block
+  if (wave < 4) {
+    if (4 * wave < M)
+      epilogue_rows_lds<1>(zown + 4 * wave * kBlockCols, kBlockCols, eco, lane, mo, nbo * kBlockCols, 4 * wave, M);
+  }
+  for (int i = 0; i < nleft; ++i) {
+    if (i > 0) {
+      __syncthreads();                                   // zleft of the previous block is read
+      if (wave >= 8) left_sum(i, threadIdx.x - 512);
+      __syncthreads();
+    }
+    int jl, nbl;
+    locate(s_left[i], jl, nbl);
+    const MemberArgs &ml = a.m[jl];
+    if (wave >= 4 && wave < 8 && 4 * (wave - 4) < M) {
+      const int r4 = 4 * (wave - 4);
+      const EpiCols ecl = epi_cols(ml, nbl * kBlockCols, lane);
+      epilogue_rows_lds<1>(zleft + r4 * kBlockCols, kBlockCols, ecl, lane, ml, nbl * kBlockCols, r4, M);
     }
   }
 }
@@ -1224,6 +1404,7 @@ constexpr LinearFn pick_kernel(int kernel) {
 
 template <int BITS>
 LinearFn pick_linear(int kernel, bool chained) {
+  if (kernel == kSpread16) return linear_spread_kernel<BITS>;
   if (kernel == kChain16x8) return linear_chain_kernel<BITS, 1, true, 8>;
   return chained ? pick_kernel<BITS, true>(kernel) : pick_kernel<BITS, false>(kernel);
 }
@@ -1231,7 +1412,8 @@ LinearFn pick_linear(int kernel, bool chained) {
 }  // namespace
 
 int launch_linear(const LinearArgs &a, int bits, int kernel, bool chained, void *stream) {
-  if (kernel < kChain16 || kernel > kTile128 || (kernel == kChain16x8 && !chained)) return (int)hipErrorInvalidValue;
+  if (kernel < kChain16 || kernel > kSpread16 || ((kernel == kChain16x8 || kernel == kSpread16) && !chained))
+    return (int)hipErrorInvalidValue;
   LinearFn fn = nullptr;
   switch (bits) {
     case 2: fn = pick_linear<2>(kernel, chained); break;
