@@ -193,7 +193,8 @@ int exl3_test_dequant(const exl3_weight_t *w, void *out_fp16, void *stream);
 int exl3_test_codebook(const void *states_u16, void *out_fp16, int64_t n, void *stream);
 
 /* exl3_test_rot_in — the rotated input Xr [M][K] fp16 (natural K order) that
- * the input rotation of `w` produces. Errors: as exl3_linear, EHIP. */
+ * the input rotation of `w` produces; xr_fp16 must be 16-byte aligned.
+ * Errors: as exl3_linear (EALIGN also for a misaligned xr_fp16), EHIP. */
 int exl3_test_rot_in(const exl3_weight_t *w, const void *x, int64_t ldx, int64_t M,
                      void *xr_fp16, void *stream);
 

@@ -467,6 +467,7 @@ int exl3_test_rot_in(const exl3_weight_t *w, const void *x, int64_t ldx, int64_t
   const int e = check_weight(w);
   if (e != EXL3_OK) return e;
   if (M < 0 || !xr_fp16 || !x || ldx < w->K) return EXL3_EINVAL;
+  if ((uintptr_t)xr_fp16 % 16 != 0 || (uintptr_t)x % 2 != 0) return EXL3_EALIGN;
   if (M == 0) return EXL3_OK;
   if ((uint64_t)M * w->K * 2 >= (uint64_t(1) << 31)) return EXL3_EINVAL;
   exl3::RotArgs ra{};

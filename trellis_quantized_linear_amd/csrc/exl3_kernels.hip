@@ -181,23 +181,6 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t u) { return __uint_as_floa
 __device__ __forceinline__ float fp16_to_f32(uint16_t u) { return (float)__builtin_bit_cast(_Float16, u); }
 __device__ __forceinline__ uint16_t f32_to_fp16(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
 
-// ------------------------------------------------------------ Hadamard
-// Unnormalised 128-point Sylvester transform of one 128-vector held by a wave,
-// element `lane` in v0 and element `lane + 64` in v1. Levels h = 1, 2, ..., 64
-// in that order; each pair (i, i+h) becomes (a+b, a-b) in fp32.
-__device__ __forceinline__ void fwht128_pair(float &v0, float &v1, int lane) {
-#pragma unroll
-  for (int h = 1; h < 64; h <<= 1) {
-    const float p0 = __shfl_xor(v0, h, 64);
-    const float p1 = __shfl_xor(v1, h, 64);
-    if (lane & h) { v0 = p0 - v0; v1 = p1 - v1; }
-    else          { v0 = v0 + p0; v1 = v1 + p1; }
-  }
-  const float a = v0, b = v1;
-  v0 = a + b;
-  v1 = a - b;
-}
-
 // ------------------------------------------------------------ epilogue
 //
 // A wave finishes 4*NQ rows of one block's Z (rows row0 .. row0 + 4NQ - 1,
@@ -352,38 +335,67 @@ __device__ __forceinline__ void epilogue_rows_lds(float *zrows, int pitch, const
   epilogue_rows<NQ>(z, ec, lane, m, col0, row0, M, (uint16_t *)zrows);
 }
 
-// Position of logical K index k inside its 8-group in slot order:
-// logical r < 4 -> 2r, r >= 4 -> 2(r-4)+1.
-__device__ __forceinline__ int slot_pos(int k) {
-  const int r = k & 7;
-  return (k & ~7) + (r < 4 ? 2 * r : 2 * (r - 4) + 1);
+// ------------------------------------------------------------ rot_in / rot_group
+//
+// Xr = fp16( FWHT128(X ⊙ suh) · 2^-4 ) per 128-chunk of K, the same
+// butterflies as the output transform: levels h = 1, 2, ..., 64 in that order,
+// each pair (i, i + h) -> (a + b, a - b) in fp32. One wave per (member, 4 rows,
+// 128-chunk): lane l (c = l % 16, g = l / 16) holds elements 8c .. 8c+7 of row
+// 4q + g, so levels 1, 2, 4 pair registers and levels 8, 16, 32, 64 pair
+// lanes c ^ 1, c ^ 2, c ^ 4, c ^ 8 of a 16-lane DPP row. Each lane loads and
+// stores 16 contiguous bytes; Xr leaves in the MFMA slot order (within each
+// group of 8: k0 k4 k1 k5 k2 k6 k3 k7), or in natural order for the test hook.
+
+// 8 consecutive 16-bit values from p (any 2-byte alignment).
+__device__ __forceinline__ u32x4 load8_u16(const uint16_t *p) {
+  if (((uintptr_t)p & 15) == 0) return *(const u32x4 *)p;
+  u32x4 r;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) r[e] = (uint32_t)p[2 * e] | ((uint32_t)p[2 * e + 1] << 16);
+  return r;
 }
 
-// ------------------------------------------------------------ rot_in / rot_group
-// One wave per (member, row, 128-chunk of K).
 __global__ __launch_bounds__(kThreads) void rot_kernel(const RotArgs a) {
   const int lane = threadIdx.x & 63;
+  const int c = lane & 15, g = lane >> 4;
   const int64_t item = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
   const int kc = a.K >> 7;
-  const int64_t per_member = (int64_t)a.M * kc;
+  const int quads = (a.M + 3) >> 2;
+  const int64_t per_member = (int64_t)quads * kc;
   if (item >= per_member * a.n_members) return;
   const int j = (int)(item / per_member);
   const int64_t rem = item - (int64_t)j * per_member;
-  const int row = (int)(rem / kc);
-  const int chunk = (int)(rem - (int64_t)row * kc);
+  const int quad = (int)(rem / kc);
+  const int chunk = (int)(rem - (int64_t)quad * kc);
+  const int row = 4 * quad + g;
+  if (row >= a.M) return;                                // no cross-lane step below mixes rows
   const uint16_t *suh = j == 0 ? a.suh[0] : (j == 1 ? a.suh[1] : a.suh[2]);
   uint16_t *xr = j == 0 ? a.xr[0] : (j == 1 ? a.xr[1] : a.xr[2]);
-  const int k0 = chunk * 128 + lane;
-  const int k1 = k0 + 64;
-  const uint16_t *xrow = a.x + (int64_t)row * a.ldx;
-  float v0 = bf16_to_f32(xrow[k0]) * fp16_to_f32(suh[k0]);
-  float v1 = bf16_to_f32(xrow[k1]) * fp16_to_f32(suh[k1]);
-  fwht128_pair(v0, v1, lane);
-  v0 = v0 * 0.0625f;
-  v1 = v1 * 0.0625f;
-  uint16_t *xrrow = xr + (int64_t)row * a.K;
-  xrrow[a.natural_order ? k0 : slot_pos(k0)] = f32_to_fp16(v0);
-  xrrow[a.natural_order ? k1 : slot_pos(k1)] = f32_to_fp16(v1);
+  const int k0 = chunk * 128 + 8 * c;
+  const u32x4 xw = load8_u16(a.x + (int64_t)row * a.ldx + k0);
+  const u32x4 sw = load8_u16(suh + k0);
+  float v[8][1];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    v[2 * e][0] = bf16_to_f32((uint16_t)(xw[e] & 0xFFFFu)) * fp16_to_f32((uint16_t)(sw[e] & 0xFFFFu));
+    v[2 * e + 1][0] = bf16_to_f32((uint16_t)(xw[e] >> 16)) * fp16_to_f32((uint16_t)(sw[e] >> 16));
+  }
+  register_level<1>(v);
+  register_level<2>(v);
+  register_level<4>(v);
+  lane_level<1>(v, c);
+  lane_level<2>(v, c);
+  lane_level<4>(v, c);
+  lane_level<8>(v, c);
+  uint16_t h[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) h[e] = f32_to_fp16(v[e][0] * 0.0625f);
+  u32x4 out;
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    out[e] = a.natural_order ? ((uint32_t)h[2 * e] | ((uint32_t)h[2 * e + 1] << 16))
+                             : ((uint32_t)h[e] | ((uint32_t)h[e + 4] << 16));
+  *(u32x4 *)(xr + (int64_t)row * a.K + k0) = out;
 }
 
 // ------------------------------------------------------------ linear
@@ -1056,30 +1068,45 @@ void linear_chain_kernel(const LinearArgs a) {
     __syncthreads();
     if (!s_last) return;
     if (threadIdx.x == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    // Sum the S partials in split order. Thread x owns fragments x, x + NT,
-    // ... (of MT * 512); their loads are issued 8 splits at a time (clamped to
-    // the last split) before they are added.
+    // Sum the S partials in split order. Thread x owns the FB fragments x,
+    // x + NT, ... (of MT * 512); the loads of all of them are issued together,
+    // B splits at a time (clamped to the last split), before they are added:
+    // one memory round trip per B splits.
+    constexpr int FB = MT * 512 / NT;
+    constexpr int B = FB <= 2 ? 16 : 8;
+    f32x4 zv[FB];
+    bool live[FB];
 #pragma unroll
-    for (int e = 0; e < MT * 512 / NT; ++e) {
+    for (int e = 0; e < FB; ++e) {
+      const int fl = (threadIdx.x + e * NT) & 63, fmt = (threadIdx.x + e * NT) >> 9;
+      live[e] = row_base + 16 * fmt + 4 * (fl >> 4) < M;
+    }
+    for (int s0 = 0; s0 < S; s0 += B) {
+      u32x4 v[FB][B];
+#pragma unroll
+      for (int u = 0; u < B; ++u) {
+        const __amdgpu_buffer_rsrc_t rp =
+            make_rsrc(partial_frag(m, min(s0 + u, S - 1), rb, nb, a.row_blocks, MT), MT * 8 * 1024);
+#pragma unroll
+        for (int e = 0; e < FB; ++e)
+          v[e][u] = live[e] ? __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                            rp, 16 * (threadIdx.x + e * NT), 0, kAgentScope))
+                            : u32x4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int e = 0; e < FB; ++e)
+#pragma unroll
+        for (int u = 0; u < B; ++u)
+          if (s0 + u < S) zv[e] = (s0 + u == 0) ? __builtin_bit_cast(f32x4, v[e][u]) : zv[e] + __builtin_bit_cast(f32x4, v[e][u]);
+    }
+#pragma unroll
+    for (int e = 0; e < FB; ++e) {
       const int f = threadIdx.x + e * NT;                // fragment index: mt, t, lane
       const int fl = f & 63, ft = (f >> 6) & 7, fmt = f >> 9;
       const int fr0 = 16 * fmt + 4 * (fl >> 4);          // first of its 4 rows in the row block
-      if (row_base + fr0 < M) {
-        f32x4 zv = f32x4{0.f, 0.f, 0.f, 0.f};
-        for (int s0 = 0; s0 < S; s0 += 8) {
-          u32x4 v[8];
+      if (live[e]) {
 #pragma unroll
-          for (int u = 0; u < 8; ++u) {
-            const __amdgpu_buffer_rsrc_t rp =
-                make_rsrc(partial_frag(m, min(s0 + u, S - 1), rb, nb, a.row_blocks, MT), MT * 8 * 1024);
-            v[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rp, 16 * f, 0, kAgentScope));
-          }
-#pragma unroll
-          for (int u = 0; u < 8; ++u)
-            if (s0 + u < S) zv = (s0 + u == 0) ? __builtin_bit_cast(f32x4, v[u]) : zv + __builtin_bit_cast(f32x4, v[u]);
-        }
-#pragma unroll
-        for (int q = 0; q < 4; ++q) zrow[(fr0 + q) * kBlockCols + 16 * ft + (fl & 15)] = zv[q];
+        for (int q = 0; q < 4; ++q) zrow[(fr0 + q) * kBlockCols + 16 * ft + (fl & 15)] = zv[e][q];
       }
     }
   }
@@ -1431,7 +1458,7 @@ int launch_linear(const LinearArgs &a, int bits, int kernel, bool chained, void 
 }
 
 int launch_rot(const RotArgs &a, void *stream) {
-  const int64_t items = (int64_t)a.n_members * a.M * (a.K / 128);
+  const int64_t items = (int64_t)a.n_members * ((a.M + 3) / 4) * (a.K / 128);
   const int64_t wgs = (items + kWaves - 1) / kWaves;
   (void)hipGetLastError();
   hipLaunchKernelGGL(rot_kernel, dim3((unsigned)wgs), dim3(kThreads), 0, (hipStream_t)stream, a);
