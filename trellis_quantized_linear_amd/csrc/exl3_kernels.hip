@@ -44,6 +44,9 @@ constexpr int kWaitVmcnt0 = 0x0F70;
 // workgroups: SC1, agent scope (written through / fetched past the XCD's
 // non-coherent L2), the same bit LLVM sets for agent-scope atomics here.
 constexpr int kAgentScope = 16;
+// Cache policy of the weight stream at up to 32 rows: non-temporal (NT), the
+// words are read once per call and should not displace the rotated input.
+constexpr int kStreamOnce = 2;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, kRsrcWord3);
@@ -649,7 +652,7 @@ __device__ __forceinline__ void load_chain_stage(ChainStage<BITS, MT> &st, __amd
     st.a[mt] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, (int)voff_a[mt], soff_a, 0));
 #pragma unroll
   for (int l = 0; l < Stream<BITS>::kLoads; ++l)
-    st.b[l] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, (int)voff_b[l], soff_b, 0));
+    st.b[l] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, (int)voff_b[l], soff_b, kStreamOnce));
 }
 
 // Copy a stage's weight bytes into LDS slot `slot` (byte address).
