@@ -201,7 +201,9 @@ int exl3_test_rot_in(const exl3_weight_t *w, const void *x, int64_t ldx, int64_t
 /* exl3_test_force — force the row tiling and launch shape (the analogue of
  * the pages' Linear.min_rows override, PR #1467 follow-up). Neither changes
  * the bits of a row:
- *   m_tiles: -1 automatic, else 1, 2, 4 or 8 16-row MFMA tiles per workgroup;
+ *   m_tiles: -1 automatic, else 1, 2, 4 or 8 16-row MFMA tiles per workgroup,
+ *            or 16: 128-row tiles two 128-column blocks wide (the automatic
+ *            choice above 128 rows; chained launches only, else as 8);
  *   chained: -1 automatic, 0 one K split per workgroup with counter exchange,
  *            1 every split of a block in one workgroup, summed in order,
  *            2 the spread launch (up to 16 rows, one S <= 15 for every

@@ -51,15 +51,15 @@ def test_rows_identical_for_every_row_count(name, K, N, bits):
 @pytest.mark.parametrize("name,K,N,bits", SHAPES[:4])
 def test_rows_identical_for_every_tiling_and_launch_shape(name, K, N, bits):
     """The min_rows analogue: force each row tiling (1, 2, 4, 8 MFMA row tiles
-    per workgroup) and each launch shape (one split per workgroup with counter
-    exchange, every split in one workgroup, and at 16 rows the spread launch)
-    at several row counts."""
+    per workgroup, and 128-row tiles two blocks wide) and each launch shape
+    (one split per workgroup with counter exchange, every split in one
+    workgroup, and at 16 rows the spread launch) at several row counts."""
     L = G.layer("tiling", name, K, N, bits)
     w = G.upload(L)
     x = G.xbits("tiling", 40, K)
     xd = G.dev_bf16(x)
     ref = G.host_u16(G.run(w, xd, M=40, tag="auto"))
-    for mt in (1, 2, 4, 8):
+    for mt in (1, 2, 4, 8, 16):
         for chained in ((0, 1, 2) if mt == 1 else (0, 1)):
             ex().exl3_test_force(mt, chained, 0)
             for M in (1, 16, 17, 40):
@@ -116,10 +116,11 @@ def test_prompt_rows_equal_decode_rows():
     assert np.array_equal(win, full[128:144])
 
 
-@pytest.mark.parametrize("M", [1, 7, 16])
+@pytest.mark.parametrize("M", [1, 7, 16, 200])
 def test_group_equals_each_member_alone(M):
     """PR #1467 exl3-midm: the q/k/v and gate/up groups equal each member's own
-    launch at 1, 7 and 16 rows."""
+    launch at 1, 7 and 16 rows, and at 200 prompt rows (two row blocks, the
+    members' tiles side by side in one launch)."""
     K = synth.HIDDEN
     x = G.xbits("group", M, K)
     xd = G.dev_bf16(x)
@@ -191,6 +192,22 @@ def test_views_equal_full_head_columns():
     b128 = G.host_u16(G.run(w.columns(240128, 8192), x128, tag="span B, 128 rows"))
     tail3 = G.host_u16(G.run(w.columns(248320 - 384, 384), x128, tag="3-block tail, 128 rows"))
     assert not np.array_equal(tail3, b128[:, -384:])
+
+
+def test_prompt_rows_of_an_odd_view_equal_full_head():
+    """Prompt rows over a view that starts at an odd block and spans an odd
+    number of blocks (65 of the 6-bit head, so it plans as the head does):
+    the 128-row tiles two blocks wide pair other blocks than in the full
+    head, and the last tile holds one block. 200 rows, bitwise against the
+    full head's columns."""
+    K, N, M = 5120, synth.VOCAB, 200
+    L = G.layer("views", "head", K, N, 6)
+    w = G.upload(L)
+    xd = G.dev_bf16(G.xbits("views-prompt", M, K, sigma=0.5))
+    full = G.host_u16(G.run(w, xd, tag="full head, 200 rows"))
+    v = G.host_u16(G.run(w.columns(128, 65 * 128), xd, tag="65-block view from block 1, 200 rows"))
+    assert ex().exl3_plan(K, 65 * 128, 6).splits == ex().exl3_plan(K, N, 6).splits
+    assert np.array_equal(v, full[:, 128:128 + 65 * 128])
 
 
 def test_counters_zero_at_rest_and_repeats_identical():

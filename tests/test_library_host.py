@@ -291,6 +291,8 @@ def test_test_force_validation(lib):
     assert lib.exl3_test_force(-1, 3, 0) == ex.EXL3_EINVAL
     assert lib.exl3_test_force(-1, -1, -1) == ex.EXL3_EINVAL
     assert lib.exl3_test_force(8, 1, 4) == ex.EXL3_OK
+    assert lib.exl3_test_force(16, 1, 0) == ex.EXL3_OK
+    assert lib.exl3_test_force(32, 1, 0) == ex.EXL3_EINVAL
 
 
 def test_dispatch_sweep_reaches_only_built_forms(lib):

@@ -111,7 +111,10 @@ constexpr int64_t kChainedMinBlocks16 = 512;
 Launch choose_launch(const MemberPlan *mp, int n, int64_t M) {
   Launch L;
   int mt = g_hooks.m_tiles;
-  if (mt != 1 && mt != 2 && mt != 4 && mt != 8) mt = M <= 16 ? 1 : M <= 32 ? 2 : M <= 64 ? 4 : 8;
+  // 16: 128-row tiles two blocks wide; automatic above 128 rows
+  const bool wide = mt == 16 || (mt == -1 && M > 128);
+  if (mt == 16) mt = 8;
+  else if (mt != 1 && mt != 2 && mt != 4 && mt != 8) mt = M <= 16 ? 1 : M <= 32 ? 2 : M <= 64 ? 4 : 8;
   L.m_tiles = mt;
   L.row_blocks = (M + 16 * mt - 1) / (16 * mt);
   bool all_single = true;
@@ -165,6 +168,7 @@ Launch choose_launch(const MemberPlan *mp, int n, int64_t M) {
            : mt == 1 ? (L.chained ? exl3::kChain16x8 : exl3::kChain16)
            : mt == 2 ? exl3::kChain32
            : mt == 4 ? exl3::kNtile64
+           : wide && L.chained ? exl3::kWide128
                      : exl3::kTile128;
   L.exchange = !L.chained || (spread && L.left_blocks > 0);
   return L;
@@ -360,7 +364,8 @@ int run_group(int32_t n_members, const exl3_weight_t *const *w, const void *x, i
       m.counters = (uint32_t *)base + counter_off;
       counter_off += (size_t)L.row_blocks * mp[j].n_blocks;
     }
-    wg += L.row_blocks * mp[j].n_blocks * m.groups;
+    wg += L.kernel == exl3::kWide128 ? L.row_blocks * ((mp[j].n_blocks + 1) / 2)
+                                     : L.row_blocks * mp[j].n_blocks * m.groups;
   }
   if (L.kernel == exl3::kSpread16) wg = L.own_blocks;
   if (wg >= (int64_t(1) << 31)) return EXL3_EINVAL;
@@ -485,7 +490,8 @@ int exl3_test_rot_in(const exl3_weight_t *w, const void *x, int64_t ldx, int64_t
 }
 
 int exl3_test_force(int32_t m_tiles, int32_t chained, int32_t splits) {
-  if (!(m_tiles == -1 || m_tiles == 1 || m_tiles == 2 || m_tiles == 4 || m_tiles == 8)) return EXL3_EINVAL;
+  if (!(m_tiles == -1 || m_tiles == 1 || m_tiles == 2 || m_tiles == 4 || m_tiles == 8 || m_tiles == 16))
+    return EXL3_EINVAL;
   if (chained < -1 || chained > 2 || splits < 0) return EXL3_EINVAL;
   g_hooks.m_tiles = m_tiles;
   g_hooks.chained = chained;

@@ -21,6 +21,8 @@
 // the group launch and rot_group return the bytes of the one-weight launch).
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "exl3_internal.h"
 
 namespace exl3 {
@@ -1373,6 +1375,273 @@ void linear_tile_kernel(const LinearArgs a) {
   }
 }
 
+// ------------------------------------------------------------ linear, 128 x 256 tiles
+//
+// Prompt rows. A workgroup computes 128 rows x two adjacent 128-column blocks
+// of one member; wave w owns all 128 rows of block w / 2, columns 64 (w % 2)
+// .. 64 (w % 2) + 63: 8 x 4 MFMA tiles, one wave per SIMD, so that each
+// decoded B operand feeds 8 MFMAs and each A operand 4. Per 32-deep chunk the
+// rotated input tile (128 rows x 64 bytes) and the two blocks' words are
+// copied from memory straight into an LDS ring (buffer loads with the LDS
+// destination: no staging registers, no LDS store instructions), kStages - 1
+// chunks ahead, one barrier per chunk. The input tile's 16-byte pieces are
+// placed with an XOR swizzle so that the operand reads (16 rows of one
+// 16-byte column per 16 lanes) hit distinct banks; each tile row of words
+// gets a slot padded to an odd multiple of 128 bytes, so the two tile rows a
+// wave reads fall in opposite halves of the banks. A wave decodes the next
+// chunk's 4 B operands between this chunk's MFMAs and re-reads each A operand
+// for the next chunk as soon as its 4 MFMAs are issued. Chains, their fold in
+// split order and the epilogue are those of every other tiling.
+
+template <int BITS>
+struct WideLds {
+  static constexpr int kA = 128 * 64;                        // input tile of one chunk
+  static constexpr int kRowBytes = 256 * BITS;               // one tile row (8 tiles) of one block
+  static constexpr int kRow = kRowBytes + 128;               // its slot
+  static constexpr int kStage = kA + 4 * kRow;               // + 2 blocks x 2 tile rows
+  static constexpr int kStages = 8;
+  static constexpr int kRing = kStages * kStage;
+  static constexpr int kZ = 2 * 128 * 132 * 4;               // epilogue: both blocks' Z, 132-float rows
+  static constexpr int kBytes = kRing > kZ ? kRing : kZ;
+  static constexpr int kRowCopies = (kRowBytes + 1023) / 1024;
+  static constexpr int kCopies = 2 + kRowCopies;             // 1 KB copies per wave and chunk
+};
+
+// s_waitcnt operand: at most n vector memory operations outstanding.
+__host__ __device__ constexpr int wait_vmcnt(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Workgroup barrier without a memory fence. LDS filled by buffer-to-LDS
+// copies is ordered by explicit vmcnt waits before it; the compiler may not
+// move memory operations across it.
+__device__ __forceinline__ void ring_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ void copy_to_lds(__amdgpu_buffer_rsrc_t r, char *dst, uint32_t voff, int soff) {
+  // 16 bytes per lane: lane l's bytes land at dst + 16 l; lanes past the
+  // buffer's num_records write zeros, inactive lanes write nothing
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)dst, 16, (int)voff, soff, 0, 0);
+}
+
+// +0 in four fresh accumulator registers. Opaque to the optimizer, which
+// otherwise merges every cleared accumulator into one register and then
+// copies all of them on every pass of the chunk loop.
+__device__ __forceinline__ f32x4 opaque_zero4() {
+  float e0, e1, e2, e3;
+  asm volatile("v_accvgpr_write_b32 %0, 0" : "=a"(e0));
+  asm volatile("v_accvgpr_write_b32 %0, 0" : "=a"(e1));
+  asm volatile("v_accvgpr_write_b32 %0, 0" : "=a"(e2));
+  asm volatile("v_accvgpr_write_b32 %0, 0" : "=a"(e3));
+  return f32x4{e0, e1, e2, e3};
+}
+
+template <int BITS>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void linear_wide_kernel(const LinearArgs a) {
+  using WL = WideLds<BITS>;
+  using TR = BitsTraits<BITS>;
+  constexpr int NS = WL::kStages;
+  constexpr int ND = TR::kDwords;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c = lane & 15, g = lane >> 4;
+
+  // Workgroup -> tile. Workgroups are dealt to the 8 XCDs in turn; each XCD
+  // takes a contiguous range of tiles, ordered by groups of 8 block pairs and
+  // within a group by row block, so the workgroups that share an L2 at a time
+  // share input rows and words.
+  const int T = a.total_wgs;
+  const int xcd = blockIdx.x & 7;
+  const int tile = xcd * (T >> 3) + min(xcd, T & 7) + (int)(blockIdx.x >> 3);
+  int j = 0;
+  if (a.n_members > 1 && tile >= a.m[1].wg_begin) j = 1;
+  if (a.n_members > 2 && tile >= a.m[2].wg_begin) j = 2;
+  const MemberArgs &m = a.m[j];
+  const int RB = a.row_blocks;
+  const int pairs = (m.n_blocks + 1) >> 1;
+  const int local = tile - m.wg_begin;
+  const int pg = local / (8 * RB);
+  const int in_g = local - pg * 8 * RB;
+  const int gp = min(8, pairs - 8 * pg);
+  const int rb = in_g / gp;
+  const int pair = 8 * pg + (in_g - rb * gp);
+  const int M = a.M, K = a.K, C = a.chunks;
+  const int row_base = rb * 128;
+  const int col0 = pair * 2 * kBlockCols;
+  const int n_blk = min(2, m.n_blocks - 2 * pair);           // 1 or 2 blocks in this pair
+
+  __shared__ __attribute__((aligned(16))) char lds[WL::kBytes];
+
+  // copies: wave w moves input pieces 64 (2w + e) + lane (e = 0, 1) and tile row
+  // slot w (block w / 2, tile row w % 2) of every chunk
+  const __amdgpu_buffer_rsrc_t ra =
+      make_rsrc(m.xr + (int64_t)row_base * K, (uint32_t)min(M - row_base, 128) * (uint32_t)K * 2u);
+  uint32_t va[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int p = 64 * (2 * wave + e) + lane;
+    const int r = p >> 2, s16 = (p & 3) ^ ((r >> 2) & 3);
+    va[e] = row_base + r < M ? (uint32_t)(r * 2 * K + 16 * s16) : kOutOfRange;
+  }
+  const __amdgpu_buffer_rsrc_t rw =
+      make_rsrc(m.words + (int64_t)2 * pair * m.block_stride, (uint32_t)(n_blk * m.block_stride));
+  const int qw = wave >> 1, hw = wave & 1;
+  uint32_t vw[WL::kRowCopies];
+  bool ow[WL::kRowCopies];
+#pragma unroll
+  for (int e = 0; e < WL::kRowCopies; ++e) {
+    const int b = 1024 * e + 16 * lane;
+    ow[e] = b < WL::kRowBytes;
+    vw[e] = (uint32_t)(qw * m.block_stride + hw * WL::kRowBytes + b);
+  }
+  auto issue_copies = [&](int chunk, char *stage) {
+#pragma unroll
+    for (int e = 0; e < 2; ++e) copy_to_lds(ra, stage + 1024 * (2 * wave + e), va[e], chunk * 64);
+#pragma unroll
+    for (int e = 0; e < WL::kRowCopies; ++e)
+      if (ow[e]) copy_to_lds(rw, stage + WL::kA + wave * WL::kRow + 1024 * e, vw[e], chunk * 512 * BITS);
+  };
+
+  // operand reads: A piece (row 16 mt + c, 16-byte column g) and the lane's
+  // word dwords of column tiles 4 (w % 2) + t of block w / 2
+  const uint32_t a_rd = (uint32_t)(64 * c + 16 * (g ^ (c >> 2)));
+  const BLane<BITS> bl = b_lane<BITS>(lane);
+  uint32_t w_rd[ND];
+#pragma unroll
+  for (int d = 0; d < ND; ++d)
+    w_rd[d] = (uint32_t)(WL::kA + 2 * qw * WL::kRow + hw * 128 * BITS + 128 * (g >> 1)) + bl.voff[d];
+  const CbConst cbc = cb_const();
+
+  auto stage_of = [&](int i) { return lds + (i & (NS - 1)) * WL::kStage; };
+  auto read_a = [&](half8 (&af)[8], const char *st) {
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) af[mt] = __builtin_bit_cast(half8, *(const u32x4 *)(st + a_rd + 1024 * mt));
+  };
+  auto read_w = [&](uint32_t (&w)[4][ND], const char *st) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int d = 0; d < ND; ++d) w[t][d] = *(const uint32_t *)(st + w_rd[d] + 32 * BITS * t);
+  };
+
+  // z = P0 + P1 + ... in split order, starting from +0: an MFMA chain that
+  // starts from +0 never ends in -0, so +0 + P0 is P0 bit for bit
+  f32x4 acc[8][4], z[8][4];
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) z[mt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int last = C - 1;
+  const int S = m.splits;
+
+  // prologue: chunks 0 .. NS - 2 in flight; chunks 0 and 1 landed
+#pragma unroll
+  for (int p = 0; p < NS - 1; ++p) issue_copies(min(p, last), stage_of(p));
+  __builtin_amdgcn_s_waitcnt(wait_vmcnt(WL::kCopies * (NS - 3)));
+  ring_barrier();
+  half8 af[8], bc[4], bn[4];
+  uint32_t wa[4][ND], wb[4][ND];
+  read_a(af, stage_of(0));
+  read_w(wa, stage_of(0));
+#pragma unroll
+  for (int t = 0; t < 4; ++t) bc[t] = decode8<BITS>(wa[t], bl.shift, cbc);
+  read_w(wa, stage_of(1));
+
+  // one chunk: MFMAs of chunk cc (A in af, B in bc; FIRST: the chain's first
+  // chunk, accumulating onto zero); meanwhile the words of chunk cc + 1 (wa)
+  // become its B operands (bn), the words of chunk cc + 2 are read (wb) and
+  // af is refilled with chunk cc + 1's A
+  auto step = [&](int cc, auto first, half8 (&bc)[4], half8 (&bn)[4], uint32_t (&wa)[4][ND],
+                  uint32_t (&wb)[4][ND]) {
+    __builtin_amdgcn_s_waitcnt(wait_vmcnt(WL::kCopies * (NS - 4)));   // this wave's copies of chunk cc + 2
+    ring_barrier();                                         // everyone's; the stage of chunk cc - 1 is free
+    issue_copies(min(cc + NS - 1, last), stage_of(cc + NS - 1));
+    read_w(wb, stage_of(cc + 2));
+    const char *nxt = stage_of(cc + 1);
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        acc[mt][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[mt], bc[t], decltype(first)::value ? f32x4{0.f, 0.f, 0.f, 0.f}
+                                                                                               : acc[mt][t], 0, 0, 0);
+      af[mt] = __builtin_bit_cast(half8, *(const u32x4 *)(nxt + a_rd + 1024 * mt));
+      if (mt & 1) bn[mt >> 1] = decode8<BITS>(wa[mt >> 1], bl.shift, cbc);
+    }
+    // issue order: each MFMA followed by about two VALU operations (the
+    // decode of the next chunk), each A operand's reload after its 4 MFMAs
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);   // VALU
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);     // LDS read
+    }
+  };
+  using First = std::integral_constant<bool, true>;
+  using Rest = std::integral_constant<bool, false>;
+  // chain s covers chunks [s C / S, (s + 1) C / S), at least one chunk; its
+  // sum is then added to z (accumulator registers read into the add
+  // directly, so z stays in place)
+  for (int sp = 0; sp < S; ++sp) {
+    const int c0 = sp * C / S, c1 = (sp + 1) * C / S;      // S * C < 2^31
+    step(c0, First{}, bc, bn, wa, wb);
+    int cc = c0 + 1;
+    for (; cc + 1 < c1; cc += 2) {
+      step(cc, Rest{}, bn, bc, wb, wa);
+      step(cc + 1, Rest{}, bc, bn, wa, wb);
+    }
+    if (cc < c1) {
+      step(cc, Rest{}, bn, bc, wb, wa);
+    } else {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        bc[t] = bn[t];
+#pragma unroll
+        for (int d = 0; d < ND; ++d) wa[t][d] = wb[t][d];
+      }
+    }
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          float v;
+          asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(acc[mt][t][q]));
+          z[mt][t][q] = z[mt][t][q] + v;
+        }
+  }
+
+  // epilogue: both blocks' Z through LDS once every copy has landed
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  __syncthreads();
+  float *zb = (float *)lds;                                  // [2][128][132]
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) zb[(qw * 128 + 16 * mt + 4 * g + q) * 132 + 64 * hw + 16 * t + c] = z[mt][t][q];
+  const EpiCols ec0 = epi_cols(m, col0, lane);
+  EpiCols ec1 = ec0;
+  if (n_blk > 1) ec1 = epi_cols(m, col0 + kBlockCols, lane);
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int grp = wave + 4 * i;                            // 16-row group: block grp / 8, rows 16 (grp % 8) ..
+    const int q = grp >> 3, r16 = 16 * (grp & 7);
+    if (q < n_blk && row_base + r16 < M)
+      epilogue_rows_lds<4>(zb + (q * 128 + r16) * 132, 132, q ? ec1 : ec0, lane, m, col0 + q * kBlockCols,
+                           row_base + r16, M);
+  }
+}
+
 // ------------------------------------------------------------ test hooks
 
 template <int BITS>
@@ -1436,13 +1705,15 @@ template <int BITS>
 LinearFn pick_linear(int kernel, bool chained) {
   if (kernel == kSpread16) return linear_spread_kernel<BITS>;
   if (kernel == kChain16x8) return linear_chain_kernel<BITS, 1, true, 8>;
+  if (kernel == kWide128) return linear_wide_kernel<BITS>;
   return chained ? pick_kernel<BITS, true>(kernel) : pick_kernel<BITS, false>(kernel);
 }
 
 }  // namespace
 
 int launch_linear(const LinearArgs &a, int bits, int kernel, bool chained, void *stream) {
-  if (kernel < kChain16 || kernel > kSpread16 || ((kernel == kChain16x8 || kernel == kSpread16) && !chained))
+  if (kernel < kChain16 || kernel > kWide128 ||
+      ((kernel == kChain16x8 || kernel == kSpread16 || kernel == kWide128) && !chained))
     return (int)hipErrorInvalidValue;
   LinearFn fn = nullptr;
   switch (bits) {
