@@ -1384,11 +1384,11 @@ void linear_tile_kernel(const LinearArgs a) {
 // rotated input tile (128 rows x 64 bytes) and the two blocks' words are
 // copied from memory straight into an LDS ring (buffer loads with the LDS
 // destination: no staging registers, no LDS store instructions), kStages - 1
-// chunks ahead, one barrier per chunk. The input tile's 16-byte pieces are
-// placed with an XOR swizzle so that the operand reads (16 rows of one
-// 16-byte column per 16 lanes) hit distinct banks; each tile row of words
-// gets a slot padded to an odd multiple of 128 bytes, so the two tile rows a
-// wave reads fall in opposite halves of the banks. A wave decodes the next
+// chunks ahead, one barrier per chunk. The input tile is stored as 8 MFMA
+// operands of 1 KB, lane l's 16 bytes at 16 l, so the operand reads are
+// linear and free of bank conflicts; each tile row of words gets a slot
+// padded to an odd multiple of 128 bytes, so the two tile rows a wave reads
+// fall in opposite halves of the banks. A wave decodes the next
 // chunk's 4 B operands between this chunk's MFMAs and re-reads each A operand
 // for the next chunk as soon as its 4 MFMAs are issued. Chains, their fold in
 // split order and the epilogue are those of every other tiling.
@@ -1476,16 +1476,16 @@ void linear_wide_kernel(const LinearArgs a) {
 
   __shared__ __attribute__((aligned(16))) char lds[WL::kBytes];
 
-  // copies: wave w moves input pieces 64 (2w + e) + lane (e = 0, 1) and tile row
-  // slot w (block w / 2, tile row w % 2) of every chunk
+  // copies: wave w moves input operands 2w + e (e = 0, 1; lane l brings row
+  // 16 (2w + e) + l % 16, 16-byte column l / 16) and tile row slot w (block
+  // w / 2, tile row w % 2) of every chunk
   const __amdgpu_buffer_rsrc_t ra =
       make_rsrc(m.xr + (int64_t)row_base * K, (uint32_t)min(M - row_base, 128) * (uint32_t)K * 2u);
   uint32_t va[2];
 #pragma unroll
   for (int e = 0; e < 2; ++e) {
-    const int p = 64 * (2 * wave + e) + lane;
-    const int r = p >> 2, s16 = (p & 3) ^ ((r >> 2) & 3);
-    va[e] = row_base + r < M ? (uint32_t)(r * 2 * K + 16 * s16) : kOutOfRange;
+    const int r = 16 * (2 * wave + e) + c;                   // operand 2w + e: rows 16 (2w + e) + l % 16
+    va[e] = row_base + r < M ? (uint32_t)(r * 2 * K + 16 * g) : kOutOfRange;
   }
   const __amdgpu_buffer_rsrc_t rw =
       make_rsrc(m.words + (int64_t)2 * pair * m.block_stride, (uint32_t)(n_blk * m.block_stride));
@@ -1506,9 +1506,10 @@ void linear_wide_kernel(const LinearArgs a) {
       if (ow[e]) copy_to_lds(rw, stage + WL::kA + wave * WL::kRow + 1024 * e, vw[e], chunk * 512 * BITS);
   };
 
-  // operand reads: A piece (row 16 mt + c, 16-byte column g) and the lane's
-  // word dwords of column tiles 4 (w % 2) + t of block w / 2
-  const uint32_t a_rd = (uint32_t)(64 * c + 16 * (g ^ (c >> 2)));
+  // operand reads: A operand mt at 1 KB mt + 16 lane (linear: no bank
+  // conflicts) and the lane's word dwords of column tiles 4 (w % 2) + t of
+  // block w / 2
+  const uint32_t a_rd = (uint32_t)(16 * lane);
   const BLane<BITS> bl = b_lane<BITS>(lane);
   uint32_t w_rd[ND];
 #pragma unroll
