@@ -164,12 +164,18 @@ Launch choose_launch(const MemberPlan *mp, int n, int64_t M) {
     // blocks and wide weights give enough workgroups by themselves.
     L.chained = all_single || M > 128 || L.row_blocks * blocks >= 256;
   }
+  // 128-row tiles: the block tiling (4 waves of 128 x 32, operands copied
+  // into an LDS ring), except exchanged splits of more than 16 chunks, which
+  // run faster on the 2 x 2 tiling
+  bool long_chains = false;
+  for (int j = 0; j < n; ++j) long_chains = long_chains || (mp[j].w->K / kChunk) > 16 * mp[j].splits;
   L.kernel = spread    ? exl3::kSpread16
            : mt == 1 ? (L.chained ? exl3::kChain16x8 : exl3::kChain16)
            : mt == 2 ? exl3::kChain32
            : mt == 4 ? exl3::kNtile64
            : wide && L.chained ? exl3::kWide128
-                     : exl3::kTile128;
+           : !L.chained && long_chains ? exl3::kTile128
+                     : exl3::kBlock128;
   L.exchange = !L.chained || (spread && L.left_blocks > 0);
   return L;
 }

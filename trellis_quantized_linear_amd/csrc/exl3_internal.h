@@ -72,6 +72,7 @@ enum LinearKernel {
   kTile128 = 4,     // 128 rows per workgroup, 2 x 2 waves of 64 x 64
   kSpread16 = 5,    // 16 rows, 16 waves: one own block per workgroup + spare waves on left blocks
   kWide128 = 6,     // 128 rows x 2 blocks per workgroup, 4 waves of 128 x 64 (chained only)
+  kBlock128 = 7,    // 128 rows x 1 block per workgroup, 4 waves of 128 x 32
 };
 
 inline int waves_per_wg(int kernel) { return kernel == kSpread16 ? 16 : kernel == kChain16x8 ? 8 : kWaves; }

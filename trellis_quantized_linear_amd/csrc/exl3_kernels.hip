@@ -1643,6 +1643,271 @@ void linear_wide_kernel(const LinearArgs a) {
   }
 }
 
+// ------------------------------------------------------------ linear, 128-row block tiles
+//
+// Up to 128 rows (and prompt launches with exchanged splits). A workgroup of
+// 4 waves computes 128 rows x one 128-column block; wave w owns all 128 rows
+// of column tiles 2w, 2w + 1 (8 x 2 MFMA tiles), so each decoded B operand
+// feeds 8 MFMAs, and two workgroups fit on a CU (two waves per SIMD). The
+// operands reach LDS as in the 128 x 256 tiling: buffer-to-LDS copies into a
+// 6-stage ring, input operands stored linearly, tile rows of words in padded
+// slots. Chained: every split of the block, folded in split order. Exchanged:
+// one split per workgroup, its partial stored in the fragment layout; the
+// block's last arriving workgroup adds the S partials in split order, resets
+// the counter and finishes the rows.
+
+template <int BITS>
+struct BlockLds {
+  static constexpr int kA = 128 * 64;                        // input tile of one chunk
+  static constexpr int kRowBytes = 256 * BITS;               // one tile row (8 tiles) of the block
+  static constexpr int kRow = kRowBytes + 128;               // its slot
+  static constexpr int kStage = kA + 2 * kRow;
+  static constexpr int kStages = 6;
+  static constexpr int kRing = kStages * kStage;
+  static constexpr int kZ = 128 * 132 * 4;                   // epilogue: the block's Z, 132-float rows
+  static constexpr int kBytes = kRing > kZ ? kRing : kZ;
+  static constexpr int kPiece = kRowBytes / 2;               // bytes of a tile row one wave copies (<= 1 KB)
+  static constexpr int kCopies = 3;                          // copies per wave and chunk: 2 input operands + a piece
+};
+
+template <int BITS, bool CHAINED>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void linear_block_kernel(const LinearArgs a) {
+  using BL = BlockLds<BITS>;
+  using TR = BitsTraits<BITS>;
+  constexpr int NS = BL::kStages;
+  constexpr int ND = TR::kDwords;
+  constexpr int TN = 2;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c = lane & 15, g = lane >> 4;
+
+  // Workgroup -> (member, row block, block, split): dealt to the 8 XCDs in
+  // turn, each XCD taking a contiguous range ordered by groups of 8 blocks,
+  // then row block, block and split.
+  const int T = a.total_wgs;
+  const int xcd = blockIdx.x & 7;
+  const int tile = xcd * (T >> 3) + min(xcd, T & 7) + (int)(blockIdx.x >> 3);
+  int j = 0;
+  if (a.n_members > 1 && tile >= a.m[1].wg_begin) j = 1;
+  if (a.n_members > 2 && tile >= a.m[2].wg_begin) j = 2;
+  const MemberArgs &m = a.m[j];
+  const int RB = a.row_blocks;
+  const int groups = m.groups;                               // 1 (chained) or S
+  const int local = tile - m.wg_begin;
+  const int pg = local / (8 * RB * groups);
+  const int in_g = local - pg * 8 * RB * groups;
+  const int gp = min(8, m.n_blocks - 8 * pg);
+  const int rb = in_g / (gp * groups);
+  const int r2 = in_g - rb * gp * groups;
+  const int nb = 8 * pg + r2 / groups;
+  const int sg = r2 - (r2 / groups) * groups;
+  const int M = a.M, K = a.K, C = a.chunks;
+  const int S = m.splits;
+  const int row_base = rb * 128;
+  const int col0 = nb * kBlockCols;
+
+  __shared__ __attribute__((aligned(16))) char lds[BL::kBytes];
+
+  // copies: wave w moves input operands 2w + e (lane l brings row
+  // 16 (2w + e) + l % 16, 16-byte column l / 16) and half w % 2 of tile row
+  // w / 2 of every chunk
+  const __amdgpu_buffer_rsrc_t ra =
+      make_rsrc(m.xr + (int64_t)row_base * K, (uint32_t)min(M - row_base, 128) * (uint32_t)K * 2u);
+  uint32_t va[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int r = 16 * (2 * wave + e) + c;
+    va[e] = row_base + r < M ? (uint32_t)(r * 2 * K + 16 * g) : kOutOfRange;
+  }
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(m.words + (int64_t)nb * m.block_stride, (uint32_t)m.block_stride);
+  const int hrow = wave >> 1, half = wave & 1;
+  const bool ow = 16 * lane < BL::kPiece;
+  const uint32_t vw = (uint32_t)(hrow * BL::kRowBytes + half * BL::kPiece + 16 * lane);
+  auto stage_of = [&](int i) { return lds + (int)((unsigned)i % NS) * BL::kStage; };
+  auto issue_copies = [&](int chunk, char *stage) {
+#pragma unroll
+    for (int e = 0; e < 2; ++e) copy_to_lds(ra, stage + 1024 * (2 * wave + e), va[e], chunk * 64);
+    if (ow) copy_to_lds(rw, stage + BL::kA + hrow * BL::kRow + half * BL::kPiece, vw, chunk * 512 * BITS);
+  };
+
+  // operand reads: A operand mt at 1 KB mt + 16 lane; the lane's word dwords
+  // of column tiles 2w + t
+  const int t0 = 2 * wave;
+  const uint32_t a_rd = (uint32_t)(16 * lane);
+  const BLane<BITS> bl = b_lane<BITS>(lane);
+  uint32_t w_rd[ND];
+#pragma unroll
+  for (int d = 0; d < ND; ++d) w_rd[d] = (uint32_t)(BL::kA + t0 * 32 * BITS + 128 * (g >> 1)) + bl.voff[d];
+  const CbConst cbc = cb_const();
+  auto read_a = [&](half8 (&af)[8], const char *st) {
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) af[mt] = __builtin_bit_cast(half8, *(const u32x4 *)(st + a_rd + 1024 * mt));
+  };
+  auto read_w = [&](uint32_t (&w)[TN][ND], const char *st) {
+#pragma unroll
+    for (int t = 0; t < TN; ++t)
+#pragma unroll
+      for (int d = 0; d < ND; ++d) w[t][d] = *(const uint32_t *)(st + w_rd[d] + 32 * BITS * t);
+  };
+
+  // chunk range: every split (chained) or split sg
+  const int cbeg = CHAINED ? 0 : (int)(sg * C / S);
+  const int cend = CHAINED ? C : (int)((sg + 1) * C / S);
+  const int last = cend - 1;
+
+  // z = P0 + P1 + ... in split order, starting from +0: an MFMA chain that
+  // starts from +0 never ends in -0, so +0 + P0 is P0 bit for bit
+  f32x4 acc[8][TN], z[8][TN];
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+    for (int t = 0; t < TN; ++t) z[mt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // prologue: chunks cbeg .. cbeg + NS - 2 in flight; cbeg and cbeg + 1 landed
+#pragma unroll
+  for (int p = 0; p < NS - 1; ++p) issue_copies(min(cbeg + p, last), stage_of(cbeg + p));
+  __builtin_amdgcn_s_waitcnt(wait_vmcnt(BL::kCopies * (NS - 3)));
+  ring_barrier();
+  half8 af[8], bc[TN], bn[TN];
+  uint32_t wa[TN][ND], wb[TN][ND];
+  read_a(af, stage_of(cbeg));
+  read_w(wa, stage_of(cbeg));
+#pragma unroll
+  for (int t = 0; t < TN; ++t) bc[t] = decode8<BITS>(wa[t], bl.shift, cbc);
+  read_w(wa, stage_of(cbeg + 1));
+
+  // one chunk: MFMAs of chunk cc (A in af, B in bc; FIRST: the chain's first
+  // chunk, accumulating onto zero); meanwhile the words of chunk cc + 1 (wa)
+  // become its B operands (bn), the words of chunk cc + 2 are read (wb) and
+  // af is refilled with chunk cc + 1's A
+  auto step = [&](int cc, auto first, half8 (&bc)[TN], half8 (&bn)[TN], uint32_t (&wa)[TN][ND],
+                  uint32_t (&wb)[TN][ND]) {
+    __builtin_amdgcn_s_waitcnt(wait_vmcnt(BL::kCopies * (NS - 4)));   // this wave's copies of chunk cc + 2
+    ring_barrier();                                         // everyone's; the stage of chunk cc - 1 is free
+    issue_copies(min(cc + NS - 1, last), stage_of(cc + NS - 1));
+    read_w(wb, stage_of(cc + 2));
+    const char *nxt = stage_of(cc + 1);
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) {
+#pragma unroll
+      for (int t = 0; t < TN; ++t)
+        acc[mt][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[mt], bc[t], decltype(first)::value ? f32x4{0.f, 0.f, 0.f, 0.f}
+                                                                                               : acc[mt][t], 0, 0, 0);
+      af[mt] = __builtin_bit_cast(half8, *(const u32x4 *)(nxt + a_rd + 1024 * mt));
+      if ((mt & 3) == 3) bn[mt >> 2] = decode8<BITS>(wa[mt >> 2], bl.shift, cbc);
+    }
+  };
+  using First = std::integral_constant<bool, true>;
+  using Rest = std::integral_constant<bool, false>;
+  auto chain = [&](int c0, int c1) {
+    step(c0, First{}, bc, bn, wa, wb);
+    int cc = c0 + 1;
+    for (; cc + 1 < c1; cc += 2) {
+      step(cc, Rest{}, bn, bc, wb, wa);
+      step(cc + 1, Rest{}, bc, bn, wa, wb);
+    }
+    if (cc < c1) {
+      step(cc, Rest{}, bn, bc, wb, wa);
+    } else {
+#pragma unroll
+      for (int t = 0; t < TN; ++t) {
+        bc[t] = bn[t];
+#pragma unroll
+        for (int d = 0; d < ND; ++d) wa[t][d] = wb[t][d];
+      }
+    }
+  };
+  auto fold = [&]() {
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+      for (int t = 0; t < TN; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float v;
+          asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(acc[mt][t][e]));
+          z[mt][t][e] = z[mt][t][e] + v;
+        }
+  };
+
+  if constexpr (CHAINED) {
+    // chain s covers chunks [s C / S, (s + 1) C / S), at least one chunk
+    for (int sp = 0; sp < S; ++sp) {
+      chain(sp * C / S, (sp + 1) * C / S);                  // S * C < 2^31
+      fold();
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+  } else {
+    chain(cbeg, cend);
+    // split sg's partial in the fragment layout, then the counter exchange
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    const __amdgpu_buffer_rsrc_t rp = make_rsrc(partial_frag(m, sg, rb, nb, RB, 8), 8 * 8 * 1024);
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+      for (int t = 0; t < TN; ++t)
+        if (row_base + 16 * mt + 4 * g < M) {
+          float v[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v[e]) : "a"(acc[mt][t][e]));
+          __builtin_amdgcn_raw_buffer_store_b128(u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]),
+                                                       __float_as_uint(v[2]), __float_as_uint(v[3])},
+                                                 rp, (mt * 8 + t0 + t) * 1024 + 16 * lane, 0, kAgentScope);
+        }
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);                 // this wave's partial stores are complete
+    __syncthreads();
+    __shared__ int s_last;
+    uint32_t *counter = m.counters + (int64_t)rb * m.n_blocks + nb;
+    if (threadIdx.x == 0) {
+      const uint32_t prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_last = prev == (uint32_t)(groups - 1);
+    }
+    __syncthreads();
+    if (!s_last) return;
+    if (threadIdx.x == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // z = P0 + P1 + ... for this wave's 16 fragments, 4 splits per batch
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+      for (int t = 0; t < TN; ++t) {
+        const int f = (mt * 8 + t0 + t) * 64 + lane;
+        if (row_base + 16 * mt + 4 * g < M) {
+          f32x4 zv = f32x4{0.f, 0.f, 0.f, 0.f};
+          for (int s0 = 0; s0 < S; s0 += 4) {
+            u32x4 v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              const __amdgpu_buffer_rsrc_t rq = make_rsrc(partial_frag(m, min(s0 + u, S - 1), rb, nb, RB, 8), 8 * 8 * 1024);
+              v[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, 16 * f, 0, kAgentScope));
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+              if (s0 + u < S) zv = zv + __builtin_bit_cast(f32x4, v[u]);
+          }
+          z[mt][t] = zv;
+        }
+      }
+  }
+
+  // epilogue: the block's Z through LDS
+  float *zb = (float *)lds;                                  // [128][132]
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+    for (int t = 0; t < TN; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) zb[(16 * mt + 4 * g + e) * 132 + 16 * (t0 + t) + c] = z[mt][t][e];
+  const EpiCols ec = epi_cols(m, col0, lane);
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r16 = 16 * (wave + 4 * i);
+    if (row_base + r16 < M) epilogue_rows_lds<4>(zb + r16 * 132, 132, ec, lane, m, col0, row_base + r16, M);
+  }
+}
+
 // ------------------------------------------------------------ test hooks
 
 template <int BITS>
@@ -1707,13 +1972,14 @@ LinearFn pick_linear(int kernel, bool chained) {
   if (kernel == kSpread16) return linear_spread_kernel<BITS>;
   if (kernel == kChain16x8) return linear_chain_kernel<BITS, 1, true, 8>;
   if (kernel == kWide128) return linear_wide_kernel<BITS>;
+  if (kernel == kBlock128) return chained ? linear_block_kernel<BITS, true> : linear_block_kernel<BITS, false>;
   return chained ? pick_kernel<BITS, true>(kernel) : pick_kernel<BITS, false>(kernel);
 }
 
 }  // namespace
 
 int launch_linear(const LinearArgs &a, int bits, int kernel, bool chained, void *stream) {
-  if (kernel < kChain16 || kernel > kWide128 ||
+  if (kernel < kChain16 || kernel > kBlock128 ||
       ((kernel == kChain16x8 || kernel == kSpread16 || kernel == kWide128) && !chained))
     return (int)hipErrorInvalidValue;
   LinearFn fn = nullptr;
