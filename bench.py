@@ -161,6 +161,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one plain 1 GiB device copy (PMC scale reference)")
+    ap.add_argument("--only", choices=SECTIONS,
+                    help="profiling aid: run one of the extra figures alone and print it (no bench line)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: the library has no multi-GPU path (asked for {args.gpus}).",
@@ -180,6 +182,9 @@ def main():
     layers = {n: synth.gen_layer("bench-27b", n, K, N, bits) for n, N in names}
     log("uploading", NCOPY, "copies of q/k/v/gate/up")
     copies = upload_copies(ex, [layers[n] for n, _ in names], NCOPY)
+    if args.only:
+        print(json.dumps(run_extras(ex, torch, synth, layers, copies, args.only)), flush=True)
+        return
     x = x_dev(M, K, 1.0, "x")
     ws_qkv = ex.Workspace().reserve(copies[0][:3], 128)
     ws_gu = ex.Workspace().reserve(copies[0][3:], 128)
@@ -266,11 +271,14 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def run_extras(ex, torch, synth, layers, copies):
+SECTIONS = ("rows", "mlp128", "prefill", "head")
+
+
+def run_extras(ex, torch, synth, layers, copies, only=None):
     extra = {}
     K = synth.HIDDEN
     # the same grouped step at M = 1 and 7 (graph replays over the copies)
-    for m in (1, 7):
+    for m in ((1, 7) if only in (None, "rows") else ()):
         xx = x_dev(m, K, 1.0, f"x{m}")
         wsa = ex.Workspace().reserve(copies[0][:3], m)
         wsb = ex.Workspace().reserve(copies[0][3:], m)
@@ -281,6 +289,8 @@ def run_extras(ex, torch, synth, layers, copies):
         extra[f"decode_step_M{m}_GBps"] = round(by / (ms * 1e-3) / 1e9, 1)
         log(f"decode step M={m}: {ms * 1e3:.2f} us, {extra[f'decode_step_M{m}_GBps']} GB/s")
 
+    if only not in (None, "mlp128"):
+        return run_extras_prefill(ex, torch, synth, copies, extra, only)
     # 27B dense SwiGLU MLP at 3.5 bpw, M = 128: {gate, up} 3-bit group + down 4-bit
     m = 128
     mlp = [synth.gen_layer("bench-mlp", "gate", K, synth.INTERMEDIATE, 3),
@@ -302,7 +312,13 @@ def run_extras(ex, torch, synth, layers, copies):
     extra["mlp_M128_GBps"] = round(by / (ms * 1e-3) / 1e9, 1)
     log(f"MLP M=128: {ms * 1e3:.1f} us, {extra['mlp_M128_TFLOPs']} TFLOP/s")
     del gs, graphs, mc
+    return run_extras_prefill(ex, torch, synth, copies, extra, only)
 
+
+def run_extras_prefill(ex, torch, synth, copies, extra, only):
+    K = synth.HIDDEN
+    if only not in (None, "prefill"):
+        return run_extras_head(ex, torch, synth, extra, only)
     # one 27B layer's six linears over an 8192-row prompt (4 bits, X ~ N(0, 0.5))
     m = 8192
     six = [copies[0][0], copies[0][1], copies[0][2], copies[0][3], copies[0][4]]
@@ -322,7 +338,13 @@ def run_extras(ex, torch, synth, layers, copies):
     extra["prefill_8192_frac_mfma"] = round(fl / (ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)
     log(f"prefill 8192 rows: {ms:.2f} ms per layer, {extra['prefill_8192_TFLOPs']} TFLOP/s")
     del ga, gb, gc, xa, xb, wsa, wsb, wsc
+    return run_extras_head(ex, torch, synth, extra, only)
 
+
+def run_extras_head(ex, torch, synth, extra, only):
+    K = synth.HIDDEN
+    if only not in (None, "head"):
+        return extra
     # the 6-bit head 5120 -> 248,320 and its span views, M = 16
     m = 16
     head = ex.Weight.from_host(synth.gen_layer("bench-head", "head", K, synth.VOCAB, 6), "cuda")
