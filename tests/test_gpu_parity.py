@@ -308,3 +308,30 @@ def test_strided_x_and_y():
     yb = G.host_u16(ybig)
     G.assert_close(yb[:, :N], O.linear_packed(L.words, K, N, 4, L.scales, L.suh, L.svh, x), what="strided")
     assert np.all(yb[:, N:] == 7)
+
+
+# ------------------------------------------------------------ widths x shapes sweep
+
+SWEEP_KN = [(128, 128), (384, 640), (1024, 2048), (4096, 384), (16384, 256)]
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 7, 8])
+def test_width_and_shape_sweep_mid_rows(bits):
+    """The width matrix (2..8 bits) over K, N in 128..16384 at mid-M rows
+    (17..128; one row count per shape, rotating with the width), every
+    launch the dispatcher picks there, sampled blocks against the oracle and
+    two rows against single-row calls bit for bit."""
+    rows_cycle = [17, 33, 64, 100, 128]
+    for i, (K, N) in enumerate(SWEEP_KN):
+        M = rows_cycle[(i + bits) % len(rows_cycle)]
+        L = G.layer("sweep", f"{K}x{N}b{bits}", K, N, bits)
+        x = G.xbits("sweep", M, K)
+        w = G.upload(L)
+        xd = G.dev_bf16(x)
+        y = G.run(w, xd, tag=f"sweep b={bits}")
+        blocks = G.sample_blocks(N // 128, k=2, seed=bits + i)
+        G.assert_close(G.gpu_blocks(y, blocks), G.oracle_blocks(L, x, blocks), what=f"sweep K={K} N={N} b={bits} M={M}")
+        full = G.host_u16(y)
+        for r in (0, M - 1):
+            one = G.host_u16(G.run(w, xd[r:r + 1], M=1, tag=f"sweep row {r}"))
+            assert np.array_equal(one[0], full[r]), (K, N, bits, M, r)
