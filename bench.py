@@ -337,6 +337,18 @@ def run_extras_prefill(ex, torch, synth, copies, extra, only):
     extra["prefill_8192_ms_per_layer"] = round(ms, 3)
     extra["prefill_8192_frac_mfma"] = round(fl / (ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)
     log(f"prefill 8192 rows: {ms:.2f} ms per layer, {extra['prefill_8192_TFLOPs']} TFLOP/s")
+    # the same layer with the opt-in single-chain prompt arithmetic (other
+    # bits than every other regime; exl3_set_prompt_arithmetic(1))
+    ex.exl3_set_prompt_arithmetic(1)
+    try:
+        fn()
+        ms1 = time_events(fn, 3)
+    finally:
+        ex.exl3_set_prompt_arithmetic(0)
+    extra["prefill_8192_single_chain_opt_in_TFLOPs"] = round(fl / (ms1 * 1e-3) / 1e12, 1)
+    extra["prefill_8192_single_chain_opt_in_ms_per_layer"] = round(ms1, 3)
+    log(f"prefill 8192 rows, opt-in single chain: {ms1:.2f} ms per layer, "
+        f"{extra['prefill_8192_single_chain_opt_in_TFLOPs']} TFLOP/s")
     del ga, gb, gc, xa, xb, wsa, wsb, wsc
     return run_extras_head(ex, torch, synth, extra, only)
 

@@ -198,6 +198,17 @@ int exl3_test_codebook(const void *states_u16, void *out_fp16, int64_t n, void *
 int exl3_test_rot_in(const exl3_weight_t *w, const void *x, int64_t ldx, int64_t M,
                      void *xr_fp16, void *stream);
 
+/* exl3_set_prompt_arithmetic — opt-in arithmetic for calls above 128 rows
+ * (the pages' rejected 64-row prompt tiles, TensorFold PR #1475, kept here
+ * as an explicit choice):
+ *   mode 0 (default): every row count, group and view gives the same bits;
+ *   mode 1: above 128 rows each output is one MFMA chain over all of K (no
+ *           K splits), on 128 x 512 tiles — faster, but its bits differ from
+ *           the other regimes' (still within the oracle tolerance). Calls of
+ *           up to 128 rows are unaffected.
+ * Process-global, not thread-safe; EXL3_EINVAL for another mode. */
+int exl3_set_prompt_arithmetic(int32_t mode);
+
 /* exl3_test_force — force the row tiling and launch shape (the analogue of
  * the pages' Linear.min_rows override, PR #1467 follow-up). Neither changes
  * the bits of a row:

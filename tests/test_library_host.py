@@ -43,7 +43,7 @@ def fake_weight(K, N, bits, base=0x10000000, block_stride=None):
 def test_exports_every_declared_symbol(lib):
     text = open(ex.HEADER).read()
     names = sorted(set(re.findall(r"^\s*(?:int|const char \*)\s*(exl3_\w+)\s*\(", text, re.M)))
-    assert len(names) == 17
+    assert len(names) == 18
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(ex._SIGNATURES), set(names) ^ set(ex._SIGNATURES)
@@ -293,6 +293,8 @@ def test_test_force_validation(lib):
     assert lib.exl3_test_force(8, 1, 4) == ex.EXL3_OK
     assert lib.exl3_test_force(16, 1, 0) == ex.EXL3_OK
     assert lib.exl3_test_force(32, 1, 0) == ex.EXL3_EINVAL
+    assert lib.exl3_set_prompt_arithmetic(2) == ex.EXL3_EINVAL
+    assert lib.exl3_set_prompt_arithmetic(0) == ex.EXL3_OK
 
 
 def test_dispatch_sweep_reaches_only_built_forms(lib):

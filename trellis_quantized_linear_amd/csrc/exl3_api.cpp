@@ -31,6 +31,10 @@ struct TestHooks {
 };
 TestHooks g_hooks;
 
+// Prompt arithmetic above 128 rows: 0 bit-stable (every regime the same
+// bits), 1 single-chain tiles (opt-in, faster, other bits). Process-global.
+int g_prompt_mode = 0;
+
 constexpr size_t kAlign = 256;
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
@@ -169,7 +173,9 @@ Launch choose_launch(const MemberPlan *mp, int n, int64_t M) {
   // run faster on the 2 x 2 tiling
   bool long_chains = false;
   for (int j = 0; j < n; ++j) long_chains = long_chains || (mp[j].w->K / kChunk) > 16 * mp[j].splits;
-  L.kernel = spread    ? exl3::kSpread16
+  const bool quad = g_prompt_mode == 1 && M > 128 && g_hooks.m_tiles == -1 && g_hooks.chained != 0;
+  L.kernel = quad      ? exl3::kQuad128
+           : spread    ? exl3::kSpread16
            : mt == 1 ? (L.chained ? exl3::kChain16x8 : exl3::kChain16)
            : mt == 2 ? exl3::kChain32
            : mt == 4 ? exl3::kNtile64
@@ -370,7 +376,8 @@ int run_group(int32_t n_members, const exl3_weight_t *const *w, const void *x, i
       m.counters = (uint32_t *)base + counter_off;
       counter_off += (size_t)L.row_blocks * mp[j].n_blocks;
     }
-    wg += L.kernel == exl3::kWide128 ? L.row_blocks * ((mp[j].n_blocks + 1) / 2)
+    wg += L.kernel == exl3::kWide128   ? L.row_blocks * ((mp[j].n_blocks + 1) / 2)
+        : L.kernel == exl3::kQuad128 ? L.row_blocks * ((mp[j].n_blocks + 3) / 4)
                                      : L.row_blocks * mp[j].n_blocks * m.groups;
   }
   if (L.kernel == exl3::kSpread16) wg = L.own_blocks;
@@ -493,6 +500,12 @@ int exl3_test_rot_in(const exl3_weight_t *w, const void *x, int64_t ldx, int64_t
   if (g_hooks.mock) { g_hooks.launches += 1; g_hooks.last_stream = stream; return EXL3_OK; }
   const int err = exl3::launch_rot(ra, stream);
   return err ? hip_fail(err) : EXL3_OK;
+}
+
+int exl3_set_prompt_arithmetic(int32_t mode) {
+  if (mode != 0 && mode != 1) return EXL3_EINVAL;
+  g_prompt_mode = mode;
+  return EXL3_OK;
 }
 
 int exl3_test_force(int32_t m_tiles, int32_t chained, int32_t splits) {

@@ -73,6 +73,7 @@ enum LinearKernel {
   kSpread16 = 5,    // 16 rows, 16 waves: one own block per workgroup + spare waves on left blocks
   kWide128 = 6,     // 128 rows x 2 blocks per workgroup, 4 waves of 128 x 64 (chained only)
   kBlock128 = 7,    // 128 rows x 1 block per workgroup, 4 waves of 128 x 32
+  kQuad128 = 8,     // opt-in single-chain prompt tiles: 128 rows x 4 blocks, 4 waves of 128 x 128
 };
 
 inline int waves_per_wg(int kernel) { return kernel == kSpread16 ? 16 : kernel == kChain16x8 ? 8 : kWaves; }

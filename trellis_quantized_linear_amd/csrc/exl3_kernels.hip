@@ -1397,13 +1397,13 @@ template <int BITS>
 struct WideLds {
   static constexpr int kA = 128 * 64;                        // input tile of one chunk
   static constexpr int kRowBytes = 256 * BITS;               // one tile row (8 tiles) of one block
-  static constexpr int kRow = kRowBytes + 128;               // its slot
+  static constexpr int kRowCopies = (kRowBytes + 1023) / 1024;
+  static constexpr int kRow = 1024 * kRowCopies + 128;       // its slot: whole 1 KB copies + 128 bytes
   static constexpr int kStage = kA + 4 * kRow;               // + 2 blocks x 2 tile rows
   static constexpr int kStages = 8;
   static constexpr int kRing = kStages * kStage;
   static constexpr int kZ = 2 * 128 * 132 * 4;               // epilogue: both blocks' Z, 132-float rows
   static constexpr int kBytes = kRing > kZ ? kRing : kZ;
-  static constexpr int kRowCopies = (kRowBytes + 1023) / 1024;
   static constexpr int kCopies = 2 + kRowCopies;             // 1 KB copies per wave and chunk
 };
 
@@ -1421,9 +1421,12 @@ __device__ __forceinline__ void ring_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// 16 bytes per lane: lane l's bytes land at dst + 16 l; lanes past the
+// buffer's num_records write zeros. Every lane of the wave takes part: a
+// lane with nothing to copy gets kOutOfRange and writes zeros into padding,
+// because under a lane-divergent branch the compiler has been seen to merge
+// two copies and take M0 from one lane (wrong LDS address for the others).
 __device__ __forceinline__ void copy_to_lds(__amdgpu_buffer_rsrc_t r, char *dst, uint32_t voff, int soff) {
-  // 16 bytes per lane: lane l's bytes land at dst + 16 l; lanes past the
-  // buffer's num_records write zeros, inactive lanes write nothing
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)dst, 16, (int)voff, soff, 0, 0);
 }
 
@@ -1491,19 +1494,17 @@ void linear_wide_kernel(const LinearArgs a) {
       make_rsrc(m.words + (int64_t)2 * pair * m.block_stride, (uint32_t)(n_blk * m.block_stride));
   const int qw = wave >> 1, hw = wave & 1;
   uint32_t vw[WL::kRowCopies];
-  bool ow[WL::kRowCopies];
 #pragma unroll
   for (int e = 0; e < WL::kRowCopies; ++e) {
     const int b = 1024 * e + 16 * lane;
-    ow[e] = b < WL::kRowBytes;
-    vw[e] = (uint32_t)(qw * m.block_stride + hw * WL::kRowBytes + b);
+    vw[e] = b < WL::kRowBytes ? (uint32_t)(qw * m.block_stride + hw * WL::kRowBytes + b) : kOutOfRange;
   }
   auto issue_copies = [&](int chunk, char *stage) {
 #pragma unroll
     for (int e = 0; e < 2; ++e) copy_to_lds(ra, stage + 1024 * (2 * wave + e), va[e], chunk * 64);
 #pragma unroll
     for (int e = 0; e < WL::kRowCopies; ++e)
-      if (ow[e]) copy_to_lds(rw, stage + WL::kA + wave * WL::kRow + 1024 * e, vw[e], chunk * 512 * BITS);
+      copy_to_lds(rw, stage + WL::kA + wave * WL::kRow + 1024 * e, vw[e], chunk * 512 * BITS);
   };
 
   // operand reads: A operand mt at 1 KB mt + 16 lane (linear: no bank
@@ -1514,7 +1515,8 @@ void linear_wide_kernel(const LinearArgs a) {
   uint32_t w_rd[ND];
 #pragma unroll
   for (int d = 0; d < ND; ++d)
-    w_rd[d] = (uint32_t)(WL::kA + 2 * qw * WL::kRow + hw * 128 * BITS + 128 * (g >> 1)) + bl.voff[d];
+    w_rd[d] = (uint32_t)(WL::kA + (2 * qw + (g >> 1)) * WL::kRow + hw * 128 * BITS) + bl.voff[d] -
+              (uint32_t)((g >> 1) * WL::kRowBytes);
   const CbConst cbc = cb_const();
 
   auto stage_of = [&](int i) { return lds + (i & (NS - 1)) * WL::kStage; };
@@ -1660,13 +1662,13 @@ template <int BITS>
 struct BlockLds {
   static constexpr int kA = 128 * 64;                        // input tile of one chunk
   static constexpr int kRowBytes = 256 * BITS;               // one tile row (8 tiles) of the block
-  static constexpr int kRow = kRowBytes + 128;               // its slot
+  static constexpr int kRow = 2048 + 128;                    // its slot: two 1 KB halves (4 tiles each) + 128 bytes
   static constexpr int kStage = kA + 2 * kRow;
   static constexpr int kStages = 6;
   static constexpr int kRing = kStages * kStage;
   static constexpr int kZ = 128 * 132 * 4;                   // epilogue: the block's Z, 132-float rows
   static constexpr int kBytes = kRing > kZ ? kRing : kZ;
-  static constexpr int kPiece = kRowBytes / 2;               // bytes of a tile row one wave copies (<= 1 KB)
+  static constexpr int kPiece = kRowBytes / 2;               // bytes of a half tile row (4 tiles, <= 1 KB)
   static constexpr int kCopies = 3;                          // copies per wave and chunk: 2 input operands + a piece
 };
 
@@ -1722,13 +1724,13 @@ void linear_block_kernel(const LinearArgs a) {
   }
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(m.words + (int64_t)nb * m.block_stride, (uint32_t)m.block_stride);
   const int hrow = wave >> 1, half = wave & 1;
-  const bool ow = 16 * lane < BL::kPiece;
-  const uint32_t vw = (uint32_t)(hrow * BL::kRowBytes + half * BL::kPiece + 16 * lane);
+  const uint32_t vw =
+      16 * lane < BL::kPiece ? (uint32_t)(hrow * BL::kRowBytes + half * BL::kPiece + 16 * lane) : kOutOfRange;
   auto stage_of = [&](int i) { return lds + (int)((unsigned)i % NS) * BL::kStage; };
   auto issue_copies = [&](int chunk, char *stage) {
 #pragma unroll
     for (int e = 0; e < 2; ++e) copy_to_lds(ra, stage + 1024 * (2 * wave + e), va[e], chunk * 64);
-    if (ow) copy_to_lds(rw, stage + BL::kA + hrow * BL::kRow + half * BL::kPiece, vw, chunk * 512 * BITS);
+    copy_to_lds(rw, stage + BL::kA + hrow * BL::kRow + half * 1024, vw, chunk * 512 * BITS);
   };
 
   // operand reads: A operand mt at 1 KB mt + 16 lane; the lane's word dwords
@@ -1738,7 +1740,9 @@ void linear_block_kernel(const LinearArgs a) {
   const BLane<BITS> bl = b_lane<BITS>(lane);
   uint32_t w_rd[ND];
 #pragma unroll
-  for (int d = 0; d < ND; ++d) w_rd[d] = (uint32_t)(BL::kA + t0 * 32 * BITS + 128 * (g >> 1)) + bl.voff[d];
+  for (int d = 0; d < ND; ++d)
+    w_rd[d] = (uint32_t)(BL::kA + (g >> 1) * BL::kRow + (t0 >> 2) * 1024 + (t0 & 3) * 32 * BITS) + bl.voff[d] -
+              (uint32_t)((g >> 1) * BL::kRowBytes);
   const CbConst cbc = cb_const();
   auto read_a = [&](half8 (&af)[8], const char *st) {
 #pragma unroll
@@ -1908,6 +1912,185 @@ void linear_block_kernel(const LinearArgs a) {
   }
 }
 
+// ------------------------------------------------------------ linear, opt-in single-chain prompt tiles
+//
+// Opt-in prompt arithmetic (not bit-equal to the other regimes): each
+// output is one MFMA chain over all of K, with no K splits and no fold, so a
+// wave can hold a 128 x 128 tile (8 x 8 MFMA tiles, 256 accumulators) and
+// each decoded B operand feeds 8 MFMAs while each A operand feeds 8. A
+// workgroup of 4 waves computes 128 rows x 4 adjacent blocks, wave w block w;
+// the operands reach LDS as in the 128 x 256 tiling (buffer-to-LDS copies,
+// input operands stored linearly, padded tile-row slots). The epilogue runs
+// on the accumulators directly (a wave holds whole 128-column rows).
+
+template <int BITS>
+struct QuadLds {
+  static constexpr int kA = 128 * 64;                        // input tile of one chunk
+  static constexpr int kRowBytes = 256 * BITS;               // one tile row (8 tiles) of one block
+  static constexpr int kRowCopies = (kRowBytes + 1023) / 1024;
+  static constexpr int kRow = 1024 * kRowCopies + 128;       // its slot: whole 1 KB copies + 128 bytes
+  static constexpr int kStage = kA + 8 * kRow;               // + 4 blocks x 2 tile rows
+  static constexpr int kScratch = 4 * 4096;                  // epilogue: 4 KB of bf16 rows per wave
+  static constexpr int kStages = (160 * 1024 - kScratch) / kStage < 8 ? (160 * 1024 - kScratch) / kStage : 8;
+  static constexpr int kRing = kStages * kStage;
+  static constexpr int kBytes = kRing + kScratch;
+  static constexpr int kCopies = 2 + 2 * kRowCopies;         // per wave and chunk: 2 input operands + 2 tile rows
+};
+
+template <int BITS>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void linear_quad_kernel(const LinearArgs a) {
+  using QL = QuadLds<BITS>;
+  using TR = BitsTraits<BITS>;
+  constexpr int NS = QL::kStages;
+  constexpr int ND = TR::kDwords;
+  static_assert(NS >= 4, "ring too shallow");
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c = lane & 15, g = lane >> 4;
+
+  // workgroup -> (member, row block, quad of blocks), dealt to the 8 XCDs in
+  // turn, each XCD a contiguous range ordered by groups of 4 quads, then row
+  // block
+  const int T = a.total_wgs;
+  const int xcd = blockIdx.x & 7;
+  const int tile = xcd * (T >> 3) + min(xcd, T & 7) + (int)(blockIdx.x >> 3);
+  int j = 0;
+  if (a.n_members > 1 && tile >= a.m[1].wg_begin) j = 1;
+  if (a.n_members > 2 && tile >= a.m[2].wg_begin) j = 2;
+  const MemberArgs &m = a.m[j];
+  const int RB = a.row_blocks;
+  const int quads = (m.n_blocks + 3) >> 2;
+  const int local = tile - m.wg_begin;
+  const int pg = local / (4 * RB);
+  const int in_g = local - pg * 4 * RB;
+  const int gp = min(4, quads - 4 * pg);
+  const int rb = in_g / gp;
+  const int quad = 4 * pg + (in_g - rb * gp);
+  const int M = a.M, K = a.K, C = a.chunks;
+  const int row_base = rb * 128;
+  const int n_blk = min(4, m.n_blocks - 4 * quad);           // 1..4 blocks in this quad
+  const int col0 = (4 * quad + wave) * kBlockCols;           // this wave's block
+
+  __shared__ __attribute__((aligned(16))) char lds[QL::kBytes];
+
+  // copies: wave w moves input operands 2w + e (lane l: row 16 (2w + e) + l % 16,
+  // 16-byte column l / 16) and both tile rows of block w
+  const __amdgpu_buffer_rsrc_t ra =
+      make_rsrc(m.xr + (int64_t)row_base * K, (uint32_t)min(M - row_base, 128) * (uint32_t)K * 2u);
+  uint32_t va[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int r = 16 * (2 * wave + e) + c;
+    va[e] = row_base + r < M ? (uint32_t)(r * 2 * K + 16 * g) : kOutOfRange;
+  }
+  const __amdgpu_buffer_rsrc_t rw =
+      make_rsrc(m.words + (int64_t)4 * quad * m.block_stride, (uint32_t)(n_blk * m.block_stride));
+  uint32_t vw[2][QL::kRowCopies];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int e = 0; e < QL::kRowCopies; ++e) {
+      const int b = 1024 * e + 16 * lane;
+      vw[h][e] = b < QL::kRowBytes ? (uint32_t)(wave * m.block_stride + h * QL::kRowBytes + b) : kOutOfRange;
+    }
+  auto stage_of = [&](int i) { return lds + (int)((unsigned)i % NS) * QL::kStage; };
+  auto issue_copies = [&](int chunk, char *stage) {
+#pragma unroll
+    for (int e = 0; e < 2; ++e) copy_to_lds(ra, stage + 1024 * (2 * wave + e), va[e], chunk * 64);
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int e = 0; e < QL::kRowCopies; ++e)
+        copy_to_lds(rw, stage + QL::kA + (2 * wave + h) * QL::kRow + 1024 * e, vw[h][e], chunk * 512 * BITS);
+  };
+
+  // operand reads: A operand mt at 1 KB mt + 16 lane; the lane's word dwords
+  // of column tile t of block w
+  const uint32_t a_rd = (uint32_t)(16 * lane);
+  const BLane<BITS> bl = b_lane<BITS>(lane);
+  uint32_t w_rd[ND];
+#pragma unroll
+  for (int d = 0; d < ND; ++d)
+    w_rd[d] = (uint32_t)(QL::kA + (2 * wave + (g >> 1)) * QL::kRow) + bl.voff[d] - (uint32_t)((g >> 1) * QL::kRowBytes);
+  const CbConst cbc = cb_const();
+  auto read_w = [&](uint32_t (&w)[8][ND], const char *st) {
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+      for (int d = 0; d < ND; ++d) w[t][d] = *(const uint32_t *)(st + w_rd[d] + 32 * BITS * t);
+  };
+
+  f32x4 acc[8][8];
+  const int last = C - 1;
+
+  // prologue: chunks 0 .. NS - 2 in flight; chunks 0 and 1 landed
+#pragma unroll
+  for (int p = 0; p < NS - 1; ++p) issue_copies(min(p, last), stage_of(p));
+  __builtin_amdgcn_s_waitcnt(wait_vmcnt(QL::kCopies * (NS - 3)));
+  ring_barrier();
+  half8 af[8], bc[8];
+  uint32_t wa[8][ND];
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt) af[mt] = __builtin_bit_cast(half8, *(const u32x4 *)(stage_of(0) + a_rd + 1024 * mt));
+  read_w(wa, stage_of(0));
+#pragma unroll
+  for (int t = 0; t < 8; ++t) bc[t] = decode8<BITS>(wa[t], bl.shift, cbc);
+  read_w(wa, stage_of(1));
+
+  // one chunk: column tile t's 8 MFMAs use bc[t], after which bc[t] is
+  // refilled with chunk cc + 1's operand (from wa); chunk cc + 1's A goes to
+  // an (read at the start, so it has the whole chunk to arrive) and the
+  // words of chunk cc + 2 to wb
+  half8 a2[8];
+  uint32_t wb[8][ND];
+  auto step = [&](int cc, auto first, half8 (&ac)[8], half8 (&an)[8], uint32_t (&wc)[8][ND], uint32_t (&wn)[8][ND]) {
+    __builtin_amdgcn_s_waitcnt(wait_vmcnt(QL::kCopies * (NS - 4)));   // this wave's copies of chunk cc + 2
+    ring_barrier();                                         // everyone's; the stage of chunk cc - 1 is free
+    issue_copies(min(cc + NS - 1, last), stage_of(cc + NS - 1));
+    const char *nxt = stage_of(cc + 1);
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) an[mt] = __builtin_bit_cast(half8, *(const u32x4 *)(nxt + a_rd + 1024 * mt));
+    read_w(wn, stage_of(cc + 2));
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt)
+        acc[mt][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ac[mt], bc[t], decltype(first)::value ? f32x4{0.f, 0.f, 0.f, 0.f}
+                                                                                               : acc[mt][t], 0, 0, 0);
+      bc[t] = decode8<BITS>(wc[t], bl.shift, cbc);
+    }
+  };
+  using First = std::integral_constant<bool, true>;
+  using Rest = std::integral_constant<bool, false>;
+  step(0, First{}, af, a2, wa, wb);
+  int cc = 1;
+  for (; cc + 1 < C; cc += 2) {
+    step(cc, Rest{}, a2, af, wb, wa);
+    step(cc + 1, Rest{}, af, a2, wa, wb);
+  }
+  if (cc < C) step(cc, Rest{}, a2, af, wb, wa);
+
+  // epilogue straight from the accumulators: row tile mt of block w
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  __syncthreads();
+  if (wave < n_blk) {
+    const EpiCols ec = epi_cols(m, col0, lane);
+    uint16_t *scratch = (uint16_t *)(lds + QL::kRing + 4096 * wave);
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) {
+      if (row_base + 16 * mt >= M) break;
+      float z[8][4];
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) z[t][e] = acc[mt][t][e];
+      epilogue_rows<4>(z, ec, lane, m, col0, row_base + 16 * mt, M, scratch);
+      wave_lds_sync();
+    }
+  }
+}
+
 // ------------------------------------------------------------ test hooks
 
 template <int BITS>
@@ -1973,14 +2156,15 @@ LinearFn pick_linear(int kernel, bool chained) {
   if (kernel == kChain16x8) return linear_chain_kernel<BITS, 1, true, 8>;
   if (kernel == kWide128) return linear_wide_kernel<BITS>;
   if (kernel == kBlock128) return chained ? linear_block_kernel<BITS, true> : linear_block_kernel<BITS, false>;
+  if (kernel == kQuad128) return linear_quad_kernel<BITS>;
   return chained ? pick_kernel<BITS, true>(kernel) : pick_kernel<BITS, false>(kernel);
 }
 
 }  // namespace
 
 int launch_linear(const LinearArgs &a, int bits, int kernel, bool chained, void *stream) {
-  if (kernel < kChain16 || kernel > kBlock128 ||
-      ((kernel == kChain16x8 || kernel == kSpread16 || kernel == kWide128) && !chained))
+  if (kernel < kChain16 || kernel > kQuad128 ||
+      ((kernel == kChain16x8 || kernel == kSpread16 || kernel == kWide128 || kernel == kQuad128) && !chained))
     return (int)hipErrorInvalidValue;
   LinearFn fn = nullptr;
   switch (bits) {

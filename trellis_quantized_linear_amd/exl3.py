@@ -77,6 +77,7 @@ _SIGNATURES = {
     "exl3_test_dequant": (ctypes.c_int, [W_P, P, P]),
     "exl3_test_codebook": (ctypes.c_int, [P, P, I64, P]),
     "exl3_test_rot_in": (ctypes.c_int, [W_P, P, I64, I64, P, P]),
+    "exl3_set_prompt_arithmetic": (ctypes.c_int, [I32]),
     "exl3_test_force": (ctypes.c_int, [I32, I32, I32]),
     "exl3_test_mock": (ctypes.c_int, [I32]),
     "exl3_test_mock_counts": (ctypes.c_int, [ctypes.POINTER(I64), ctypes.POINTER(I64), ctypes.POINTER(I64), PP]),
@@ -272,6 +273,12 @@ def exl3_test_rot_in(w: Weight, x, out, stream=None, M: Optional[int] = None):
     _check(lib().exl3_test_rot_in(ctypes.byref(w.desc), _ptr(x), x.stride(0), M, _ptr(out),
                                   _stream_handle(stream)), "exl3_test_rot_in")
     return out
+
+
+def exl3_set_prompt_arithmetic(mode: int):
+    """0: bit-stable prompt rows (default); 1: opt-in single-chain prompt tiles
+    above 128 rows (faster, other bits)."""
+    _check(lib().exl3_set_prompt_arithmetic(mode), "exl3_set_prompt_arithmetic")
 
 
 def exl3_test_force(m_tiles: int = -1, chained: int = -1, splits: int = 0):
