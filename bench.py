@@ -3,8 +3,10 @@
 
 A step is one pass of the whole hot path over one batch: for the 27B
 decode-row grouped linear (K = 5120, 4 bits, M = 16) it is the {q, k, v}
-group and the {gate, up} group, each as one rotation launch and one linear
-launch (trellis decode + MFMA contraction + split-K exchange + epilogue).
+group and the {gate, up} group, each one exl3_linear_group call: a rotation
+launch and a linear launch (trellis decode + MFMA contraction + split-K
+exchange + epilogue). The same step with the opt-in in-launch rotation (one
+launch per group) is timed beside it.
 Steps cycle through 8 distinct copies of the weights (8 x 110 MB) so each
 step streams its weights from HBM rather than from the 256 MB last-level
 cache. The timed steps replay HIP graphs of the step (the library's calls
@@ -72,8 +74,9 @@ class Group:
         self.ex.exl3_linear_rotated(self.w, self.y, self.ws, self.M)
 
     def call(self):
-        self.rotate()
-        self.linear()
+        """The group call (rotation + linear; one launch with the opt-in
+        in-launch rotation at up to 32 rows)."""
+        self.ex.exl3_linear_group(self.w, self.x, self.y, self.ws, M=self.M)
 
 
 def capture(fn):
@@ -221,6 +224,26 @@ def main():
     value = step_bytes / (ms_step * 1e-3) / 1e9
     log(f"step {ms_step * 1e3:.2f} us, {step_bytes / 1e6:.2f} MB -> {value:.1f} GB/s")
 
+    # the same step with the rotation inside each group's linear launch (opt-in;
+    # an extra figure, so that profiles of --no-extra runs see one kernel form)
+    ms1 = None
+    if not args.no_extra:
+        ex.exl3_test_fuse_rotation(True)
+        try:
+            graphs1 = [capture(lambda g1=g1, g2=g2: (g1.call(), g2.call())) for g1, g2 in steps]
+            for c, gr in enumerate(graphs1):
+                gr.replay()
+                torch.cuda.synchronize()
+                got = steps[c][0].y + steps[c][1].y
+                assert all(torch.equal(a.view(torch.int16), b.view(torch.int16)) for a, b in zip(got, ref[c])), \
+                    "one-launch step differs from the two-launch step"
+            ms1 = time_events(lambda: [g.replay() for g in graphs1], 20) / NCOPY
+        finally:
+            ex.exl3_test_fuse_rotation(False)
+        log(f"one-launch step (rotation inside the linear) {ms1 * 1e3:.2f} us -> "
+            f"{step_bytes / (ms1 * 1e-3) / 1e9:.1f} GB/s")
+        del graphs1
+
     # dominant kernel: the {gate, up} linear launch, back-to-back over the copies
     gu = [s[1] for s in steps]
     for g in gu:
@@ -256,6 +279,9 @@ def main():
         torch.cuda.synchronize()
         extra["copy_calibration_bytes"] = {"read": 1 << 30, "write": 1 << 30}
 
+    if ms1 is not None:
+        extra["step_rotation_in_launch_us"] = round(ms1 * 1e3, 2)
+        extra["step_rotation_in_launch_GBps"] = round(step_bytes / (ms1 * 1e-3) / 1e9, 1)
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",

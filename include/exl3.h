@@ -119,7 +119,9 @@ int exl3_weight_columns(const exl3_weight_t *parent, int64_t col_from, int64_t n
                         exl3_weight_t *view);
 
 /* exl3_workspace_need — bytes of workspace (and of its counter region) that
- * one call of exl3_linear_group with these members at M rows needs. Sizing a
+ * one call of exl3_linear_group with these members at M rows needs. The
+ * counter region holds the split counters and, for calls of up to 32 rows,
+ * the rotated-input chunk flags; all are zero between calls. Sizing a
  * workspace for the largest M it will see covers every smaller M.
  * Errors: as exl3_linear_group's argument checks. */
 int exl3_workspace_need(int32_t n_members, const exl3_weight_t *const *w, int64_t M,
@@ -143,9 +145,10 @@ int exl3_workspace_reset(const exl3_workspace_t *ws, void *stream);
 /* exl3_linear — Y[M x N] = rot_out(dequant(W) . rot_in(X)) for one weight or
  * view. M == 0 returns EXL3_OK and launches nothing. Two launches on
  * `stream`: the input rotation, then the linear (decode + MFMA + split-K
- * exchange + epilogue). Never allocates, memsets or synchronises, so it may
- * be captured in a HIP graph. Calls that run concurrently (other streams)
- * must use different workspaces.
+ * exchange + epilogue); see exl3_test_fuse_rotation for the one-launch form
+ * at up to 32 rows. Never allocates, memsets or synchronises, so it may be
+ * captured in a HIP graph. Calls that run concurrently (other streams) must
+ * use different workspaces.
  * Errors: EINVAL, EALIGN, EBITS, EWORKSPACE, EHIP. */
 int exl3_linear(const exl3_weight_t *w, const void *x, int64_t ldx, int64_t M,
                 void *y, int64_t ldy, const exl3_workspace_t *ws, void *stream);
@@ -208,6 +211,20 @@ int exl3_test_rot_in(const exl3_weight_t *w, const void *x, int64_t ldx, int64_t
  *           up to 128 rows are unaffected.
  * Process-global, not thread-safe; EXL3_EINVAL for another mode. */
 int exl3_set_prompt_arithmetic(int32_t mode);
+
+/* exl3_test_fuse_rotation — on = 1: exl3_linear and exl3_linear_group calls
+ * of up to 32 rows (the 16- and 32-row launches of one row block) run as ONE
+ * launch: its first workgroups write the rotated input into the workspace
+ * and flag each 128-column chunk, and every chain waits for the flags of the
+ * chunks it reads before reading them (the launch-gap removal the pages get
+ * from programmatic dependent launch, PR #1467, "What this changes"; every
+ * dependent read waits, as its merge review asks). on = 0 (default): a
+ * rotation launch of its own; on MI355X the in-launch wait costs more than
+ * the launch it removes. spin_limit: polls a wave makes of an unwritten
+ * chunk's flag before it rotates that chunk itself (-1: the default, 1024; 0
+ * makes every wave that finds a chunk unwritten rotate it itself, which
+ * exercises that path). Neither setting changes bits. Errors: EINVAL. */
+int exl3_test_fuse_rotation(int32_t on, int32_t spin_limit);
 
 /* exl3_test_force — force the row tiling and launch shape (the analogue of
  * the pages' Linear.min_rows override, PR #1467 follow-up). Neither changes

@@ -43,7 +43,7 @@ def fake_weight(K, N, bits, base=0x10000000, block_stride=None):
 def test_exports_every_declared_symbol(lib):
     text = open(ex.HEADER).read()
     names = sorted(set(re.findall(r"^\s*(?:int|const char \*)\s*(exl3_\w+)\s*\(", text, re.M)))
-    assert len(names) == 18
+    assert len(names) == 19
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(ex._SIGNATURES), set(names) ^ set(ex._SIGNATURES)
@@ -278,6 +278,49 @@ def test_rotate_and_linear_rotated_are_one_launch_each(lib):
     assert lib.exl3_rotate(2, arr, None, 5120, 16, ctypes.byref(ws), None) == ex.EXL3_EINVAL
     assert lib.exl3_linear_rotated(2, arr, 16, None, ld, ctypes.byref(ws), None) == ex.EXL3_EINVAL
     assert lib.exl3_linear_rotated(2, arr, 16, ys, ld, None, None) == ex.EXL3_EWORKSPACE
+
+
+def test_rotation_runs_inside_the_linear_launch_up_to_32_rows(lib):
+    """Launch-gap removal (PR #1467, "What this changes": the rotations and
+    decode-row linears chained without a gap), opt-in: with it on, a call of
+    up to 32 rows is one launch and above that two; off (the default), two
+    everywhere. The counter region holds the chunk flags either way (one word
+    per member and 128 columns of K, plus a count)."""
+    ex.exl3_test_mock(True)
+    a = fake_weight(5120, 6144, 4)
+    b = fake_weight(5120, 1024, 4, base=0x50000000)
+    arr = ex._wlist([a, b, b])
+    ys = (ctypes.c_void_p * 3)(0x80000000, 0x90000000, 0xA0000000)
+    ld = (ctypes.c_int64 * 3)(6144, 1024, 1024)
+    need, cb = ex.exl3_workspace_need([a, b, b], 300)
+    ws = ex.exl3_workspace_t(0x20000000, need, cb)
+
+    def launches(M):
+        assert lib.exl3_linear_group(3, arr, 0x30000000, 5120, M, ys, ld, ctypes.byref(ws), None) == 0
+        return ex.exl3_test_mock_counts()[0]
+
+    for M in (1, 16, 32, 33):
+        assert launches(M) == 2, M
+    ex.exl3_test_fuse_rotation(True)
+    try:
+        for M in (1, 7, 16, 17, 32):
+            assert launches(M) == 1, M
+        for M in (33, 64, 128, 300):
+            assert launches(M) == 2, M
+        # the two-phase calls never fuse
+        assert lib.exl3_rotate(3, arr, 0x30000000, 5120, 16, ctypes.byref(ws), None) == 0
+        assert lib.exl3_linear_rotated(3, arr, 16, ys, ld, ctypes.byref(ws), None) == 0
+        assert ex.exl3_test_mock_counts()[0] == 2
+    finally:
+        ex.exl3_test_fuse_rotation(False)
+    # flags: 3 members x 40 chunks + the count, on top of the split counters
+    # of the 16-row exchanged launch (64 blocks, counters of one row block)
+    _, cb16 = ex.exl3_workspace_need([a, b, b], 16)
+    assert cb16 >= 4 * (64 + 1 + 3 * 40)
+    assert lib.exl3_test_fuse_rotation(2, -1) == ex.EXL3_EINVAL
+    assert lib.exl3_test_fuse_rotation(1, -2) == ex.EXL3_EINVAL
+    assert lib.exl3_test_fuse_rotation(1, 0) == ex.EXL3_OK
+    assert lib.exl3_test_fuse_rotation(0, -1) == ex.EXL3_OK
 
 
 def test_strerror_covers_every_code(lib):

@@ -31,6 +31,15 @@ struct TestHooks {
 };
 TestHooks g_hooks;
 
+// Input rotation inside the linear launch at up to 32 rows (1: where the
+// launch allows it, 0: always a rotation launch of its own; 0 by default, as
+// the in-launch dependency costs more than the launch it removes on MI355X),
+// and the polls a wave spends on an unwritten chunk of Xr before it rotates
+// the chunk itself.
+int g_fuse_rotation = 0;
+constexpr int kDefaultSpinLimit = 1024;
+int g_spin_limit = kDefaultSpinLimit;
+
 // Prompt arithmetic above 128 rows: 0 bit-stable (every regime the same
 // bits), 1 single-chain tiles (opt-in, faster, other bits). Process-global.
 int g_prompt_mode = 0;
@@ -92,6 +101,7 @@ struct Launch {
   int64_t row_blocks;
   int64_t own_blocks = 0;   // spread launch
   int64_t left_blocks = 0;  // spread launch
+  bool can_fuse = false;    // the kernel can rotate the input itself (one row block of at most 32 rows)
 };
 
 // CUs of the current device (256 on MI355X; 256 when no device answers).
@@ -183,11 +193,15 @@ Launch choose_launch(const MemberPlan *mp, int n, int64_t M) {
            : !L.chained && long_chains ? exl3::kTile128
                      : exl3::kBlock128;
   L.exchange = !L.chained || (spread && L.left_blocks > 0);
+  L.can_fuse = L.row_blocks == 1 &&
+               (L.kernel == exl3::kSpread16 || L.kernel == exl3::kChain16 || L.kernel == exl3::kChain32) &&
+               exl3::fused_sync_words(n, mp[0].w->K) - 1 <= exl3::kMaxFusedFlags;
   return L;
 }
 
 struct Layout {
-  size_t counters;          // uint32 counters used
+  size_t counters;          // uint32 words of the counter region used: split counters, then the sync words
+  size_t sync_at;           // first sync word of a fused launch
   size_t xr_bytes[kMaxMembers];
   size_t part_bytes[kMaxMembers];
   size_t rest;              // bytes after the counter region
@@ -205,6 +219,8 @@ Layout layout_for(const MemberPlan *mp, int n, int64_t M, int64_t K, const Launc
     }
     lay.rest += lay.xr_bytes[j] + lay.part_bytes[j];
   }
+  lay.sync_at = lay.counters;
+  if (L.can_fuse) lay.counters += (size_t)exl3::fused_sync_words(n, K);
   return lay;
 }
 
@@ -282,10 +298,12 @@ int exl3_workspace_need(int32_t n_members, const exl3_weight_t *const *w, int64_
   const int e = check_group(n_members, w, M, mp);
   if (e != EXL3_OK) return e;
   size_t rest = 0, cb = 0;
-  // sizes grow with M inside each regime; the regime boundaries and M itself
-  // bound every smaller call. The counter region sits at a fixed offset, so
-  // the largest counter need and the largest rest add up.
-  const int64_t probes[3] = {std::min<int64_t>(M, 16), std::min<int64_t>(M, 128), M};
+  // sizes grow with M inside each regime; the regime boundaries (16 and 32
+  // rows: the 16- and 32-row tilings, which also hold the rotation flags;
+  // 128: the mid-M tilings) and M itself bound every smaller call. The
+  // counter region sits at a fixed offset, so the largest counter need and
+  // the largest rest add up.
+  const int64_t probes[4] = {std::min<int64_t>(M, 16), std::min<int64_t>(M, 32), std::min<int64_t>(M, 128), M};
   for (int64_t p : probes)
     if (p > 0) call_need(mp, n_members, p, &rest, &cb);
   *counter_bytes = cb;
@@ -397,6 +415,16 @@ int run_group(int32_t n_members, const exl3_weight_t *const *w, const void *x, i
   la.row_blocks = (int32_t)L.row_blocks;
   la.total_wgs = (int32_t)wg;
 
+  // both phases in one launch: the linear kernel rotates the input itself
+  const bool fuse = phases == (kRotate | kLinear) && L.can_fuse && g_fuse_rotation == 1;
+  if (fuse) {
+    la.x = (const uint16_t *)x;
+    la.ldx = ldx;
+    la.sync = (uint32_t *)base + lay.sync_at;
+    la.spin_limit = g_spin_limit;
+    for (int j = 0; j < n_members; ++j) la.m[j].suh = (const uint16_t *)w[j]->suh;
+    phases = kLinear;
+  }
   if (g_hooks.mock) {
     g_hooks.launches += ((phases & kRotate) ? 1 : 0) + ((phases & kLinear) ? 1 : 0);
     g_hooks.last_stream = stream;
@@ -505,6 +533,13 @@ int exl3_test_rot_in(const exl3_weight_t *w, const void *x, int64_t ldx, int64_t
 int exl3_set_prompt_arithmetic(int32_t mode) {
   if (mode != 0 && mode != 1) return EXL3_EINVAL;
   g_prompt_mode = mode;
+  return EXL3_OK;
+}
+
+int exl3_test_fuse_rotation(int32_t on, int32_t spin_limit) {
+  if ((on != 0 && on != 1) || spin_limit < -1) return EXL3_EINVAL;
+  g_fuse_rotation = on;
+  g_spin_limit = spin_limit == -1 ? kDefaultSpinLimit : spin_limit;
   return EXL3_OK;
 }
 

@@ -19,6 +19,7 @@ struct MemberArgs {
   const uint16_t *scales;     // fp16[N]
   const uint16_t *svh;        // fp16[N]
   const uint16_t *xr;         // rotated input [M][K], fp16, slot order
+  const uint16_t *suh;        // fp16[K] input signs (read when the rotation is fused)
   uint16_t *y;                // bf16 [M][ldy]
   float *partials;            // [S][M][N] fp32, or null when chained
   uint32_t *counters;         // [row_blocks][n_blocks], or null when chained
@@ -42,7 +43,21 @@ struct LinearArgs {
   int32_t total_wgs;
   int32_t own_blocks;         // spread launch: blocks owned by one workgroup each (= total_wgs)
   int32_t left_blocks;        // spread launch: blocks whose splits go to spare waves
+  // Fused input rotation (decode and 32-row launches): the launch itself
+  // writes every member's Xr from x before its chains read it. sync[0]
+  // counts finished workgroups; sync[1 + j * K/128 + k] says that member j's
+  // 128-column chunk k of Xr is written. All of them are zero at rest: the
+  // last workgroup to finish clears them.
+  const uint16_t *x;          // bf16 [M][ldx], or null: Xr was written by a rotation launch
+  int64_t ldx;
+  uint32_t *sync;
+  int32_t spin_limit;         // polls of an unwritten chunk's flag before a wave rotates it itself
 };
+
+// Words of the sync region of a fused launch.
+inline int64_t fused_sync_words(int n_members, int64_t K) { return 1 + (int64_t)n_members * (K / 128); }
+// Largest sync region a fused launch uses (flags of one workgroup's clear pass).
+constexpr int64_t kMaxFusedFlags = 1024;
 
 struct RotArgs {
   const uint16_t *x;          // bf16 [M][ldx]

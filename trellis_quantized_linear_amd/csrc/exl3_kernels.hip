@@ -360,25 +360,10 @@ __device__ __forceinline__ u32x4 load8_u16(const uint16_t *p) {
   return r;
 }
 
-__global__ __launch_bounds__(kThreads) void rot_kernel(const RotArgs a) {
-  const int lane = threadIdx.x & 63;
-  const int c = lane & 15, g = lane >> 4;
-  const int64_t item = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
-  const int kc = a.K >> 7;
-  const int quads = (a.M + 3) >> 2;
-  const int64_t per_member = (int64_t)quads * kc;
-  if (item >= per_member * a.n_members) return;
-  const int j = (int)(item / per_member);
-  const int64_t rem = item - (int64_t)j * per_member;
-  const int quad = (int)(rem / kc);
-  const int chunk = (int)(rem - (int64_t)quad * kc);
-  const int row = 4 * quad + g;
-  if (row >= a.M) return;                                // no cross-lane step below mixes rows
-  const uint16_t *suh = j == 0 ? a.suh[0] : (j == 1 ? a.suh[1] : a.suh[2]);
-  uint16_t *xr = j == 0 ? a.xr[0] : (j == 1 ? a.xr[1] : a.xr[2]);
-  const int k0 = chunk * 128 + 8 * c;
-  const u32x4 xw = load8_u16(a.x + (int64_t)row * a.ldx + k0);
-  const u32x4 sw = load8_u16(suh + k0);
+// Lane (c, g)'s 8 outputs of one row from its 8 inputs xw (bf16, columns
+// 128 k + 8c .. +7) and their signs sw, packed for one 16-byte store at
+// xr + row * K + 128 k + 8c.
+__device__ __forceinline__ u32x4 rot_lane(const u32x4 xw, const u32x4 sw, int c, bool natural) {
   float v[8][1];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
@@ -398,9 +383,123 @@ __global__ __launch_bounds__(kThreads) void rot_kernel(const RotArgs a) {
   u32x4 out;
 #pragma unroll
   for (int e = 0; e < 4; ++e)
-    out[e] = a.natural_order ? ((uint32_t)h[2 * e] | ((uint32_t)h[2 * e + 1] << 16))
-                             : ((uint32_t)h[e] | ((uint32_t)h[e + 4] << 16));
+    out[e] = natural ? ((uint32_t)h[2 * e] | ((uint32_t)h[2 * e + 1] << 16))
+                     : ((uint32_t)h[e] | ((uint32_t)h[e + 4] << 16));
+  return out;
+}
+
+__global__ __launch_bounds__(kThreads) void rot_kernel(const RotArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int c = lane & 15, g = lane >> 4;
+  const int64_t item = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
+  const int kc = a.K >> 7;
+  const int quads = (a.M + 3) >> 2;
+  const int64_t per_member = (int64_t)quads * kc;
+  if (item >= per_member * a.n_members) return;
+  const int j = (int)(item / per_member);
+  const int64_t rem = item - (int64_t)j * per_member;
+  const int quad = (int)(rem / kc);
+  const int chunk = (int)(rem - (int64_t)quad * kc);
+  const int row = 4 * quad + g;
+  if (row >= a.M) return;                                // no cross-lane step below mixes rows
+  const uint16_t *suh = j == 0 ? a.suh[0] : (j == 1 ? a.suh[1] : a.suh[2]);
+  uint16_t *xr = j == 0 ? a.xr[0] : (j == 1 ? a.xr[1] : a.xr[2]);
+  const int k0 = chunk * 128 + 8 * c;
+  const u32x4 out = rot_lane(load8_u16(a.x + (int64_t)row * a.ldx + k0), load8_u16(suh + k0), c, a.natural_order != 0);
   *(u32x4 *)(xr + (int64_t)row * a.K + k0) = out;
+}
+
+// ------------------------------------------------------------ rot_in inside a decode-row linear launch
+//
+// At up to 32 rows the rotation is a few microseconds of latency and almost
+// no work, so the linear launch does it itself instead of a launch of its
+// own. Member j's chunk k (128 columns of Xr, all M rows) is one item;
+// item i = j * K/128 + k belongs to the wave with global index
+// wave * gridDim.x + blockIdx.x == i (mod all waves), i.e. to the first
+// dispatched workgroups. The owner writes the item with stores that reach
+// the agent's coherence point, waits for them, and then sets the item's flag.
+// A wave about to read Xr for chunks [c0, c1) first issues its weight loads,
+// then polls the flags of the items they span (one flag per lane); no wave
+// reads an item's lines before its flag is set or it wrote them itself, so no
+// cache holds them stale. After spin_limit polls a wave rotates the items
+// still unflagged itself (the same bits as their owner), so a launch whose
+// workgroups are not all resident still ends. Each workgroup counts itself
+// done once all its waves are past their last poll; the last one clears the
+// flags and the count, which are thus zero at rest, as the split counters.
+
+// Member j's chunk k of Xr for rows 0 .. M-1 (at most 4 Q rows): one wave,
+// all of the lane's loads before any arithmetic; rows past M reread row
+// M - 1 and are not stored (out-of-range buffer stores are dropped).
+template <int Q>
+__device__ __forceinline__ void rot_item(const LinearArgs &a, int j, int k, int lane) {
+  const MemberArgs &m = a.m[j];
+  const int c = lane & 15, g = lane >> 4;
+  const int M = a.M;
+  const int k0 = k * 128 + 8 * c;
+  u32x4 xw[Q];
+#pragma unroll
+  for (int q = 0; q < Q; ++q) xw[q] = load8_u16(a.x + (int64_t)min(4 * q + g, M - 1) * a.ldx + k0);
+  const u32x4 sw = load8_u16(m.suh + k0);
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(m.xr, (uint32_t)((uint64_t)M * a.K * 2));
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    const int row = 4 * q + g;
+    const uint32_t off = row < M ? (uint32_t)(((int64_t)row * a.K + k0) * 2) : kOutOfRange;
+    __builtin_amdgcn_raw_buffer_store_b128(rot_lane(xw[q], sw, c, false), rx, (int)off, 0, kAgentScope);
+  }
+}
+
+// The items this wave owns, then their flags.
+template <int Q>
+__device__ __forceinline__ void rot_produce(const LinearArgs &a, int wave, int lane) {
+  const int kc = a.K >> 7;
+  const int items = a.n_members * kc;
+  const int all = (int)(gridDim.x * (blockDim.x >> 6));
+  for (int i = wave * (int)gridDim.x + (int)blockIdx.x; i < items; i += all) {
+    const int j = i / kc;
+    rot_item<Q>(a, j, i - j * kc, lane);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);             // the item's stores are complete
+    if (lane == 0) __hip_atomic_store(a.sync + 1 + i, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// Member j's items k0 .. k1 are in Xr when this returns.
+template <int Q>
+__device__ __forceinline__ void rot_wait(const LinearArgs &a, int j, int k0, int k1, int lane) {
+  const uint32_t *flags = a.sync + 1 + j * (a.K >> 7);
+  for (int kb = k0; kb <= k1; kb += 64) {
+    const int k = kb + lane;
+    for (int polls = 0;; ++polls) {
+      const uint32_t v = k <= k1 ? __hip_atomic_load(flags + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 1u;
+      uint64_t missing = __builtin_amdgcn_ballot_w64(v == 0u);
+      if (missing == 0) break;
+      if (polls >= a.spin_limit) {
+        while (missing) {
+          rot_item<Q>(a, j, kb + __builtin_ctzll(missing), lane);
+          missing &= missing - 1;
+        }
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+  }
+  asm volatile("" ::: "memory");
+}
+
+// One thread per workgroup, once every wave of it is past its last poll and
+// its own items are flagged: true for the launch's last workgroup.
+__device__ __forceinline__ bool rot_count_done(const LinearArgs &a) {
+  return __hip_atomic_fetch_add(a.sync, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+         (uint32_t)(gridDim.x - 1);
+}
+
+// Every thread of the last workgroup: flags and count back to zero.
+__device__ __forceinline__ void rot_clear(const LinearArgs &a) {
+  const int n = a.n_members * (a.K >> 7);
+  for (int i = threadIdx.x; i < n; i += blockDim.x)
+    __hip_atomic_store(a.sync + 1 + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (threadIdx.x == 0) __hip_atomic_store(a.sync, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ------------------------------------------------------------ linear
@@ -745,13 +844,20 @@ __device__ __forceinline__ ChainCtx<BITS, MT> chain_ctx(const MemberArgs &m, int
   return x;
 }
 
+// No wait before the chain's first rotated-input loads.
+struct NoWait {
+  __device__ void operator()() const {}
+};
+
 // One K-split chain: chunks [c0, c1) of the block over all 8 column tiles and
 // MT 16-row tiles, accumulated from zero in ascending chunk order. Chunk i of
 // the chain uses register stage i % P and LDS slot i % 2 of the wave's
 // region `wlds`; the next chunk is copied to LDS before chunk i is decoded.
-template <int BITS, int MT, int P>
+// With `fused` the first P chunks' weight loads go out before ready(), which
+// returns once the chain's part of Xr is written, and their Xr loads after.
+template <int BITS, int MT, int P, typename Ready = NoWait>
 __device__ __forceinline__ void run_chain(f32x4 (&acc)[MT][8], int c0, int c1, char *wlds,
-                                          const ChainCtx<BITS, MT> &x) {
+                                          const ChainCtx<BITS, MT> &x, bool fused = false, Ready ready = Ready{}) {
   using SB = Stream<BITS>;
   static_assert(P % 2 == 0, "the chunk loop unrolls by P, a multiple of the 2 LDS slots");
 #pragma unroll
@@ -761,10 +867,30 @@ __device__ __forceinline__ void run_chain(f32x4 (&acc)[MT][8], int c0, int c1, c
   const int n = c1 - c0;
   const int last = c1 - 1;
   ChainStage<BITS, MT> st[P];
+  if (fused) {
 #pragma unroll
-  for (int p = 0; p < P; ++p) {
-    load_chain_stage<BITS, MT>(st[p], x.ra, x.rb, x.voff_a, x.voff_b, min(c0 + p, last));
+    for (int p = 0; p < P; ++p)
+#pragma unroll
+      for (int l = 0; l < SB::kLoads; ++l)
+        st[p].b[l] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                   x.rb, (int)x.voff_b[l], min(c0 + p, last) * SB::kChunkBytes,
+                                                   kStreamOnce));
     __builtin_amdgcn_sched_barrier(0);
+    ready();
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int p = 0; p < P; ++p)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        st[p].a[mt] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                    x.ra, (int)x.voff_a[mt], min(c0 + p, last) * 64, 0));
+    __builtin_amdgcn_sched_barrier(0);
+  } else {
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      load_chain_stage<BITS, MT>(st[p], x.ra, x.rb, x.voff_a, x.voff_b, min(c0 + p, last));
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
   stage_to_lds<BITS, MT>(st[0], wlds, x.wr_off, x.wrap_off);
   // per chunk: read the staged chunk's words, stage the next chunk into the
@@ -835,9 +961,12 @@ void linear_spread_kernel(const LinearArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[kLds];
   __shared__ int s_left[W];                              // left blocks this workgroup finishes
   __shared__ int s_nleft;
+  __shared__ int s_clear;
   char *wlds = lds + wave * SB::kWave;
   if (threadIdx.x == 0) s_nleft = 0;
+  const bool fused = a.x != nullptr;
   __syncthreads();
+  if (fused) rot_produce<4>(a, wave, lane);
 
   // member j and block nb of launch block gb (members' blocks are consecutive)
   auto locate = [&](int gb, int &jj, int &nb) {
@@ -854,7 +983,8 @@ void linear_spread_kernel(const LinearArgs a) {
   if (wave >= spare) {
     const int sp = wave - spare;
     const ChainCtx<BITS, 1> x = chain_ctx<BITS, 1>(mo, M, K, nbo, 0, lane);
-    run_chain<BITS, 1, P>(acc, (int)(((int64_t)sp * C) / S), (int)(((int64_t)(sp + 1) * C) / S), wlds, x);
+    const int c0 = (int)(((int64_t)sp * C) / S), c1 = (int)(((int64_t)(sp + 1) * C) / S);
+    run_chain<BITS, 1, P>(acc, c0, c1, wlds, x, fused, [&] { rot_wait<4>(a, jo, c0 >> 2, (c1 - 1) >> 2, lane); });
   } else {
     const int unit = u * spare + wave;
     if (unit < a.left_blocks * S) {
@@ -864,7 +994,8 @@ void linear_spread_kernel(const LinearArgs a) {
       locate(gb, jl, nbl);
       const MemberArgs &ml = a.m[jl];
       const ChainCtx<BITS, 1> x = chain_ctx<BITS, 1>(ml, M, K, nbl, 0, lane);
-      run_chain<BITS, 1, P>(acc, (int)(((int64_t)sp * C) / S), (int)(((int64_t)(sp + 1) * C) / S), wlds, x);
+      const int c0 = (int)(((int64_t)sp * C) / S), c1 = (int)(((int64_t)(sp + 1) * C) / S);
+      run_chain<BITS, 1, P>(acc, c0, c1, wlds, x, fused, [&] { rot_wait<4>(a, jl, c0 >> 2, (c1 - 1) >> 2, lane); });
       // the split's partial, agent scope, then the arrival (see the exchanged launch)
       const __amdgpu_buffer_rsrc_t rp = make_rsrc(partial_frag(ml, sp, 0, nbl, 1, 1), 8 * 1024);
       if (4 * g < M) {
@@ -886,6 +1017,7 @@ void linear_spread_kernel(const LinearArgs a) {
   }
   const EpiCols eco = epi_cols(mo, nbo * kBlockCols, lane);
   __syncthreads();                                       // staging is free; the left list is final
+  if (fused && threadIdx.x == 0) s_clear = rot_count_done(a);
 
   float *pbuf = (float *)lds;                            // [S][16][128]
   float *zown = (float *)(lds + kFold);                  // [16][128]
@@ -899,6 +1031,7 @@ void linear_spread_kernel(const LinearArgs a) {
   }
   const int nleft = s_nleft;
   __syncthreads();
+  if (fused && s_clear) rot_clear(a);
   // Waves 0..7 fold the own block (P_0 + P_1 + ... in split order, 4 of its
   // 2048 values per thread); waves 8..15 meanwhile add up the first left
   // block's S partials in split order (fragment f = thread - 512: column
@@ -1000,6 +1133,11 @@ void linear_chain_kernel(const LinearArgs a) {
 
   const ChainCtx<BITS, MT> x = chain_ctx<BITS, MT>(m, M, K, nb, row_base, lane);
   const int c = lane & 15, g = lane >> 4;
+  // one row block (row_base == 0); the 8-wave form (weights of many blocks,
+  // where a rotation launch costs little) would spill with the fused prologue
+  const bool fused = W != 8 && a.x != nullptr;
+  __shared__ int s_clear;
+  if (fused) rot_produce<4 * MT>(a, wave, lane);
 
   const int s_first = CHAINED ? wave : W * sg + wave;
   const int rounds = CHAINED ? (S + W - 1) / W : 1;
@@ -1013,7 +1151,9 @@ void linear_chain_kernel(const LinearArgs a) {
     if (active) {
       // in 128 VGPRs (W = 8) only 2 chunks of more than two 128-bit loads fit
       constexpr int P = (W == 8 && SB::kLoads > 2) ? 2 : ChainDepth<MT>::P;
-      run_chain<BITS, MT, P>(acc, (int)(((int64_t)s * C) / S), (int)(((int64_t)(s + 1) * C) / S), wlds, x);
+      const int c0 = (int)(((int64_t)s * C) / S), c1 = (int)(((int64_t)(s + 1) * C) / S);
+      run_chain<BITS, MT, P>(acc, c0, c1, wlds, x, fused,
+                             [&] { rot_wait<4 * MT>(a, j, c0 >> 2, (c1 - 1) >> 2, lane); });
     }
     if constexpr (CHAINED) {
       // fold this round's chains into the running sum in split order
@@ -1059,6 +1199,8 @@ void linear_chain_kernel(const LinearArgs a) {
   const EpiCols ec = epi_cols(m, col0, lane);
 
   if constexpr (CHAINED) {
+    // every wave is past the last round's fold barriers, hence its last poll
+    if (fused && threadIdx.x == 0) s_clear = rot_count_done(a);
 #pragma unroll
     for (int e = 0; e < R * kBlockCols / NT; ++e) zrow[threadIdx.x + e * NT] = zsum[e];
   } else {
@@ -1068,9 +1210,11 @@ void linear_chain_kernel(const LinearArgs a) {
     uint32_t *counter = m.counters + (int64_t)rb * m.n_blocks + nb;
     if (threadIdx.x == 0) {
       const uint32_t prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (fused) s_clear = rot_count_done(a);
       s_last = prev == (uint32_t)(groups - 1);
     }
     __syncthreads();
+    if (fused && s_clear) rot_clear(a);
     if (!s_last) return;
     if (threadIdx.x == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     // Sum the S partials in split order. Thread x owns the FB fragments x,
@@ -1116,6 +1260,7 @@ void linear_chain_kernel(const LinearArgs a) {
     }
   }
   __syncthreads();
+  if (CHAINED && fused && s_clear) rot_clear(a);
   // 4 rows per wave and pass
   for (int r4 = 4 * wave; r4 < R && row_base + r4 < M; r4 += 4 * W)
     epilogue_rows_lds<1>(zrow + r4 * kBlockCols, kBlockCols, ec, lane, m, col0, row_base + r4, M);

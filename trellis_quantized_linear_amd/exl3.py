@@ -79,6 +79,7 @@ _SIGNATURES = {
     "exl3_test_rot_in": (ctypes.c_int, [W_P, P, I64, I64, P, P]),
     "exl3_set_prompt_arithmetic": (ctypes.c_int, [I32]),
     "exl3_test_force": (ctypes.c_int, [I32, I32, I32]),
+    "exl3_test_fuse_rotation": (ctypes.c_int, [I32, I32]),
     "exl3_test_mock": (ctypes.c_int, [I32]),
     "exl3_test_mock_counts": (ctypes.c_int, [ctypes.POINTER(I64), ctypes.POINTER(I64), ctypes.POINTER(I64), PP]),
 }
@@ -283,6 +284,13 @@ def exl3_set_prompt_arithmetic(mode: int):
 
 def exl3_test_force(m_tiles: int = -1, chained: int = -1, splits: int = 0):
     _check(lib().exl3_test_force(m_tiles, chained, splits), "exl3_test_force")
+
+
+def exl3_test_fuse_rotation(on: bool, spin_limit: int = -1):
+    """on: rotate the input inside the linear launch at up to 32 rows (off by
+    default); spin_limit: flag polls before a wave rotates a chunk itself
+    (-1: the default)."""
+    _check(lib().exl3_test_fuse_rotation(1 if on else 0, spin_limit), "exl3_test_fuse_rotation")
 
 
 def exl3_test_mock(on: bool):
