@@ -9,9 +9,11 @@ exchange + epilogue). The same step with the opt-in in-launch rotation (one
 launch per group) is timed beside it.
 Steps cycle through 8 distinct copies of the weights (8 x 110 MB) so each
 step streams its weights from HBM rather than from the 256 MB last-level
-cache. The timed steps replay HIP graphs of the step (the library's calls
-allocate and memset nothing, so they capture), bracketed by a device
-synchronisation on both sides.
+cache. The timed steps replay a HIP graph of 8 consecutive steps, one per
+weight copy, as a model's decode graph holds its layers back to back (the
+library's calls allocate and memset nothing, so they capture), bracketed by
+a device synchronisation on both sides; the same steps replayed as one graph
+each are reported beside it.
 
 Printed: one JSON line with the weight-stream GB/s of the step (`value`),
 the roofline of the dominant kernel (the {gate, up} linear launch, timed with
@@ -211,18 +213,42 @@ def main():
         assert all(torch.equal(a.view(torch.int16), b.view(torch.int16)) for a, b in zip(got, ref[c])), \
             "graph replay differs from the eager call"
 
-    for i in range(args.warmup):
-        graphs[i % NCOPY].replay()
+    # The timed steps: replays of one graph holding NCOPY consecutive steps (one
+    # per weight copy), as a model's decode graph holds its layers back to
+    # back; a remainder of K mod NCOPY steps replays one-step graphs.
+    multi = capture(lambda: [(g1.call(), g2.call()) for g1, g2 in steps])
+    multi.replay()
+    torch.cuda.synchronize()
+    for c in range(NCOPY):
+        got = steps[c][0].y + steps[c][1].y
+        assert all(torch.equal(a.view(torch.int16), b.view(torch.int16)) for a, b in zip(got, ref[c])), \
+            "multi-step graph replay differs from the eager call"
+
+    def run_steps(k):
+        for _ in range(k // NCOPY):
+            multi.replay()
+        for i in range(k % NCOPY):
+            graphs[i].replay()
+
+    run_steps(args.warmup)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        graphs[i % NCOPY].replay()
+    run_steps(args.steps)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     ms_step = dt * 1e3 / args.steps
     step_bytes = alg_bytes(copies[0][:3], M) + alg_bytes(copies[0][3:], M)
     value = step_bytes / (ms_step * 1e-3) / 1e9
     log(f"step {ms_step * 1e3:.2f} us, {step_bytes / 1e6:.2f} MB -> {value:.1f} GB/s")
+    # the same steps as one graph replay each
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        graphs[i % NCOPY].replay()
+    torch.cuda.synchronize()
+    ms_step_single = (time.perf_counter() - t0) * 1e3 / args.steps
+    log(f"step as one graph replay each: {ms_step_single * 1e3:.2f} us -> "
+        f"{step_bytes / (ms_step_single * 1e-3) / 1e9:.1f} GB/s")
 
     # the same step with the rotation inside each group's linear launch (opt-in;
     # an extra figure, so that profiles of --no-extra runs see one kernel form)
@@ -230,19 +256,19 @@ def main():
     if not args.no_extra:
         ex.exl3_test_fuse_rotation(True)
         try:
-            graphs1 = [capture(lambda g1=g1, g2=g2: (g1.call(), g2.call())) for g1, g2 in steps]
-            for c, gr in enumerate(graphs1):
-                gr.replay()
-                torch.cuda.synchronize()
+            multi1 = capture(lambda: [(g1.call(), g2.call()) for g1, g2 in steps])
+            multi1.replay()
+            torch.cuda.synchronize()
+            for c in range(NCOPY):
                 got = steps[c][0].y + steps[c][1].y
                 assert all(torch.equal(a.view(torch.int16), b.view(torch.int16)) for a, b in zip(got, ref[c])), \
                     "one-launch step differs from the two-launch step"
-            ms1 = time_events(lambda: [g.replay() for g in graphs1], 20) / NCOPY
+            ms1 = time_events(multi1.replay, 25) / NCOPY
         finally:
             ex.exl3_test_fuse_rotation(False)
         log(f"one-launch step (rotation inside the linear) {ms1 * 1e3:.2f} us -> "
             f"{step_bytes / (ms1 * 1e-3) / 1e9:.1f} GB/s")
-        del graphs1
+        del multi1
 
     # dominant kernel: the {gate, up} linear launch, back-to-back over the copies
     gu = [s[1] for s in steps]
@@ -279,6 +305,8 @@ def main():
         torch.cuda.synchronize()
         extra["copy_calibration_bytes"] = {"read": 1 << 30, "write": 1 << 30}
 
+    extra["step_one_graph_replay_each_us"] = round(ms_step_single * 1e3, 2)
+    extra["step_one_graph_replay_each_GBps"] = round(step_bytes / (ms_step_single * 1e-3) / 1e9, 1)
     if ms1 is not None:
         extra["step_rotation_in_launch_us"] = round(ms1 * 1e3, 2)
         extra["step_rotation_in_launch_GBps"] = round(step_bytes / (ms1 * 1e-3) / 1e9, 1)
@@ -309,8 +337,8 @@ def run_extras(ex, torch, synth, layers, copies, only=None):
         wsa = ex.Workspace().reserve(copies[0][:3], m)
         wsb = ex.Workspace().reserve(copies[0][3:], m)
         gs = [(Group(ex, c[:3], xx, m, wsa), Group(ex, c[3:], xx, m, wsb)) for c in copies]
-        graphs = [capture(lambda a=a, b=b: (a.call(), b.call())) for a, b in gs]
-        ms = time_events(lambda: [g.replay() for g in graphs], 10) / len(graphs)
+        multi = capture(lambda: [(a.call(), b.call()) for a, b in gs])
+        ms = time_events(multi.replay, 25) / len(gs)
         by = alg_bytes(copies[0][:3], m) + alg_bytes(copies[0][3:], m)
         extra[f"decode_step_M{m}_GBps"] = round(by / (ms * 1e-3) / 1e9, 1)
         log(f"decode step M={m}: {ms * 1e3:.2f} us, {extra[f'decode_step_M{m}_GBps']} GB/s")
@@ -328,8 +356,8 @@ def run_extras(ex, torch, synth, layers, copies, only=None):
     wsa = ex.Workspace().reserve(mc[0][:2], m)
     wsb = ex.Workspace().reserve(mc[0][2:], m)
     gs = [(Group(ex, c[:2], xa, m, wsa), Group(ex, c[2:], xb, m, wsb)) for c in mc]
-    graphs = [capture(lambda a=a, b=b: (a.call(), b.call())) for a, b in gs]
-    ms = time_events(lambda: [g.replay() for g in graphs], 10) / len(graphs)
+    multi = capture(lambda: [(a.call(), b.call()) for a, b in gs])
+    ms = time_events(multi.replay, 10) / len(gs)
     fl = flops(mc[0], m)
     by = alg_bytes(mc[0][:2], m) + alg_bytes(mc[0][2:], m)
     extra["mlp_M128_TFLOPs"] = round(fl / (ms * 1e-3) / 1e12, 1)
@@ -337,7 +365,7 @@ def run_extras(ex, torch, synth, layers, copies, only=None):
     extra["mlp_M128_frac_mfma"] = round(fl / (ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)
     extra["mlp_M128_GBps"] = round(by / (ms * 1e-3) / 1e9, 1)
     log(f"MLP M=128: {ms * 1e3:.1f} us, {extra['mlp_M128_TFLOPs']} TFLOP/s")
-    del gs, graphs, mc
+    del gs, multi, mc
     return run_extras_prefill(ex, torch, synth, copies, extra, only)
 
 
