@@ -408,6 +408,8 @@ int run_group(int32_t n_members, const exl3_weight_t *const *w, const void *x, i
   ra.K = (int32_t)K;
   ra.n_members = n_members;
   ra.natural_order = 0;
+  // the spread launch reads Xr chunk-major, every other launch row-major
+  ra.chunk_major = L.kernel == exl3::kSpread16 ? 1 : 0;
   la.n_members = n_members;
   la.M = (int32_t)M;
   la.K = (int32_t)K;
@@ -525,6 +527,7 @@ int exl3_test_rot_in(const exl3_weight_t *w, const void *x, int64_t ldx, int64_t
   ra.suh[0] = (const uint16_t *)w->suh;
   ra.xr[0] = (uint16_t *)xr_fp16;
   ra.natural_order = 1;
+  ra.chunk_major = 0;
   if (g_hooks.mock) { g_hooks.launches += 1; g_hooks.last_stream = stream; return EXL3_OK; }
   const int err = exl3::launch_rot(ra, stream);
   return err ? hip_fail(err) : EXL3_OK;

@@ -18,7 +18,8 @@ struct MemberArgs {
   const uint8_t *words;       // first byte of this member's first block
   const uint16_t *scales;     // fp16[N]
   const uint16_t *svh;        // fp16[N]
-  const uint16_t *xr;         // rotated input [M][K], fp16, slot order
+  const uint16_t *xr;         // rotated input, fp16, slot order: [M][K], or [K/32][M][32] (chunk-major)
+                              // for the spread launch
   const uint16_t *suh;        // fp16[K] input signs (read when the rotation is fused)
   uint16_t *y;                // bf16 [M][ldy]
   float *partials;            // [S][M][N] fp32, or null when chained
@@ -68,6 +69,8 @@ struct RotArgs {
   int32_t K;
   int32_t n_members;
   int32_t natural_order;      // 1: natural K order (test hook), 0: MFMA slot order
+  int32_t chunk_major;        // 1: Xr element (row, k) at ((k / 32) * M + row) * 32 + k % 32
+                              // (the layout the spread launch reads), 0: row * K + k
 };
 
 struct DequantArgs {
