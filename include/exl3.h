@@ -236,7 +236,10 @@ int exl3_test_fuse_rotation(int32_t on, int32_t spin_limit);
  *            1 every split of a block in one workgroup, summed in order,
  *            2 the spread launch (up to 16 rows, one S <= 15 for every
  *            member; otherwise as 1): a 16-wave workgroup per owned block,
- *            its spare waves taking splits of the remaining blocks.
+ *            its spare waves taking splits of the remaining blocks,
+ *            3 as 0, with each split on two waves of 4 column tiles (16-row
+ *            tiles; the automatic choice when 16-row exchanged launches have
+ *            at most one split chain per SIMD).
  * `splits` (0 = the plan's) overrides S and DOES change bits: it is the
  * planted control "another K split". */
 int exl3_test_force(int32_t m_tiles, int32_t chained, int32_t splits);

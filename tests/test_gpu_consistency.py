@@ -53,14 +53,15 @@ def test_rows_identical_for_every_tiling_and_launch_shape(name, K, N, bits):
     """The min_rows analogue: force each row tiling (1, 2, 4, 8 MFMA row tiles
     per workgroup, and 128-row tiles two blocks wide) and each launch shape
     (one split per workgroup with counter exchange, every split in one
-    workgroup, and at 16 rows the spread launch) at several row counts."""
+    workgroup, and at 16 rows the spread launch and the exchange with each
+    split on two waves of 4 column tiles) at several row counts."""
     L = G.layer("tiling", name, K, N, bits)
     w = G.upload(L)
     x = G.xbits("tiling", 40, K)
     xd = G.dev_bf16(x)
     ref = G.host_u16(G.run(w, xd, M=40, tag="auto"))
     for mt in (1, 2, 4, 8, 16):
-        for chained in ((0, 1, 2) if mt == 1 else (0, 1)):
+        for chained in ((0, 1, 2, 3) if mt == 1 else (0, 1)):
             ex().exl3_test_force(mt, chained, 0)
             for M in (1, 16, 17, 40):
                 y = G.host_u16(G.run(w, xd, M=M, tag=f"forced m_tiles={mt} chained={chained}"))

@@ -8,7 +8,8 @@ chunks it reads, and after a bounded number of polls rotates a missing chunk
 itself. Checked:
 
 * fused == two launches, byte for byte, for every decode launch form that
-  fuses (spread, exchanged 16 rows, 32 rows chained and exchanged), groups of
+  fuses (spread, exchanged 16 rows with one or two waves per split, 32 rows
+  chained and exchanged), groups of
   one to three members, three widths, and a chain that spans more than 64
   chunks (one split over K = 17408);
 * the fallback (spin limit 0: a wave that finds a chunk unflagged rotates it
@@ -61,6 +62,7 @@ CASES = [
     ("32 rows chained", 5120, (1024,), 4, (24, 32), (2, 1, 0)),
     ("16 rows exchanged, one split over K=17408", 17408, (1024,), 4, (3, 16), (1, 0, 1)),
     ("16 rows exchanged, 2 bits", 1024, (512, 256, 384), 2, (2, 15), (1, 0, 0)),
+    ("16 rows, column halves, 6 bits", 5120, (1024, 2048), 6, (4, 16), (1, 3, 0)),
 ]
 
 

@@ -331,7 +331,8 @@ def test_strerror_covers_every_code(lib):
 
 def test_test_force_validation(lib):
     assert lib.exl3_test_force(3, -1, 0) == ex.EXL3_EINVAL
-    assert lib.exl3_test_force(-1, 3, 0) == ex.EXL3_EINVAL
+    assert lib.exl3_test_force(-1, 4, 0) == ex.EXL3_EINVAL
+    assert lib.exl3_test_force(1, 3, 0) == ex.EXL3_OK
     assert lib.exl3_test_force(-1, -1, -1) == ex.EXL3_EINVAL
     assert lib.exl3_test_force(8, 1, 4) == ex.EXL3_OK
     assert lib.exl3_test_force(16, 1, 0) == ex.EXL3_OK

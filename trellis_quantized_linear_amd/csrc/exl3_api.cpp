@@ -146,8 +146,8 @@ Launch choose_launch(const MemberPlan *mp, int n, int64_t M) {
   const int64_t ncu = cu_count();
   L.exchange = false;
   bool spread = false;
-  if (g_hooks.chained >= 0 && g_hooks.chained <= 2) {
-    L.chained = g_hooks.chained != 0;
+  if (g_hooks.chained >= 0 && g_hooks.chained <= 3) {
+    L.chained = g_hooks.chained == 1 || g_hooks.chained == 2;
     if (g_hooks.chained == 2 && mt == 1 && L.row_blocks == 1 && s_uniform > 0) {
       // forced: as many left blocks as the spare waves can take
       spread = true;
@@ -184,9 +184,16 @@ Launch choose_launch(const MemberPlan *mp, int n, int64_t M) {
   bool long_chains = false;
   for (int j = 0; j < n; ++j) long_chains = long_chains || (mp[j].w->K / kChunk) > 16 * mp[j].splits;
   const bool quad = g_prompt_mode == 1 && M > 128 && g_hooks.m_tiles == -1 && g_hooks.chained != 0;
+  // 16-row exchanged launches of at most one split chain per SIMD run each
+  // chain on two waves (4 column tiles each): a lone wave per SIMD leaves
+  // the decode's latency exposed
+  int64_t chains = 0;
+  for (int j = 0; j < n; ++j) chains += L.row_blocks * mp[j].n_blocks * mp[j].splits;
+  const bool halves = mt == 1 && !L.chained &&
+                      (g_hooks.chained == 3 || (g_hooks.chained == -1 && chains <= 4 * ncu));
   L.kernel = quad      ? exl3::kQuad128
            : spread    ? exl3::kSpread16
-           : mt == 1 ? (L.chained ? exl3::kChain16x8 : exl3::kChain16)
+           : mt == 1 ? (L.chained ? exl3::kChain16x8 : halves ? exl3::kChain16H : exl3::kChain16)
            : mt == 2 ? exl3::kChain32
            : mt == 4 ? exl3::kNtile64
            : wide && L.chained ? exl3::kWide128
@@ -194,7 +201,8 @@ Launch choose_launch(const MemberPlan *mp, int n, int64_t M) {
                      : exl3::kBlock128;
   L.exchange = !L.chained || (spread && L.left_blocks > 0);
   L.can_fuse = L.row_blocks == 1 &&
-               (L.kernel == exl3::kSpread16 || L.kernel == exl3::kChain16 || L.kernel == exl3::kChain32) &&
+               (L.kernel == exl3::kSpread16 || L.kernel == exl3::kChain16 || L.kernel == exl3::kChain16H ||
+                L.kernel == exl3::kChain32) &&
                exl3::fused_sync_words(n, mp[0].w->K) - 1 <= exl3::kMaxFusedFlags;
   return L;
 }
@@ -549,7 +557,7 @@ int exl3_test_fuse_rotation(int32_t on, int32_t spin_limit) {
 int exl3_test_force(int32_t m_tiles, int32_t chained, int32_t splits) {
   if (!(m_tiles == -1 || m_tiles == 1 || m_tiles == 2 || m_tiles == 4 || m_tiles == 8 || m_tiles == 16))
     return EXL3_EINVAL;
-  if (chained < -1 || chained > 2 || splits < 0) return EXL3_EINVAL;
+  if (chained < -1 || chained > 3 || splits < 0) return EXL3_EINVAL;
   g_hooks.m_tiles = m_tiles;
   g_hooks.chained = chained;
   g_hooks.splits = splits;

@@ -92,17 +92,22 @@ enum LinearKernel {
   kWide128 = 6,     // 128 rows x 2 blocks per workgroup, 4 waves of 128 x 64 (chained only)
   kBlock128 = 7,    // 128 rows x 1 block per workgroup, 4 waves of 128 x 32
   kQuad128 = 8,     // opt-in single-chain prompt tiles: 128 rows x 4 blocks, 4 waves of 128 x 128
+  kChain16H = 9,    // 16 rows, 8 waves, exchanged: two waves per split, 4 column tiles each
 };
 
-inline int waves_per_wg(int kernel) { return kernel == kSpread16 ? 16 : kernel == kChain16x8 ? 8 : kWaves; }
+inline int waves_per_wg(int kernel) {
+  return kernel == kSpread16 ? 16 : (kernel == kChain16x8 || kernel == kChain16H) ? 8 : kWaves;
+}
 inline int threads_per_wg(int kernel) { return 64 * waves_per_wg(kernel); }
 
 // Arrivals per (row block, column block) of a launch: one when every split of
 // a block runs in one workgroup; else ceil(S / W) workgroups for the 16- and
-// 32-row tilings (one split per wave, W waves) and S for the 64- and 128-row
-// tilings (one split per workgroup).
+// 32-row tilings (one split per wave, W waves; two waves per split in the
+// column-halves form) and S for the 64- and 128-row tilings (one split per
+// workgroup).
 inline int groups_per_block(int splits, int kernel, bool chained) {
   if (chained) return 1;
+  if (kernel == kChain16H) return (splits + 3) / 4;
   return kernel <= kChain32 ? (splits + waves_per_wg(kernel) - 1) / waves_per_wg(kernel) : splits;
 }
 

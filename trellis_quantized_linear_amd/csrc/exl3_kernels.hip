@@ -735,70 +735,73 @@ __global__ __launch_bounds__(kThreads) void linear_ntile_kernel(const LinearArgs
 // one chunk ahead of the decode; a wave's region is its own, so no barrier is
 // needed.
 
-template <int BITS>
+// A wave streams CT column tiles of each chunk's two tile rows: all 8 (one
+// wave per split), or 4 (two waves per split, each with half the columns).
+template <int BITS, int CT = 8>
 struct Stream {
-  static constexpr int kChunkBytes = 512 * BITS;                 // 16 tiles
+  static constexpr int kFullChunkBytes = 512 * BITS;             // 16 tiles: the chunk's bytes in memory
+  static constexpr int kChunkBytes = 64 * CT * BITS;             // the wave's 2 CT tiles
   static constexpr int kLoads = (kChunkBytes + 1023) / 1024;     // 128-bit loads per chunk
   static constexpr int kStride = 32 * BITS + 16;                 // padded tile in LDS
-  static constexpr int kSlot = 16 * kStride + 16;                // 16 tiles + a dump for idle lanes
+  static constexpr int kSlot = 2 * CT * kStride + 16;            // the tiles + a dump for idle lanes
   static constexpr int kWave = 2 * kSlot;                        // double buffer
 };
 
 template <int MT>
 struct ChainDepth { static constexpr int P = 4; };   // chunks in flight per wave
 
-template <int BITS, int MT>
+template <int BITS, int MT, int CT = 8>
 struct ChainStage {
   u32x4 a[MT];
-  u32x4 b[Stream<BITS>::kLoads];
+  u32x4 b[Stream<BITS, CT>::kLoads];
 };
 
-template <int BITS, int MT>
-__device__ __forceinline__ void load_chain_stage(ChainStage<BITS, MT> &st, __amdgpu_buffer_rsrc_t ra,
+template <int BITS, int MT, int CT = 8>
+__device__ __forceinline__ void load_chain_stage(ChainStage<BITS, MT, CT> &st, __amdgpu_buffer_rsrc_t ra,
                                                  __amdgpu_buffer_rsrc_t rb, const uint32_t (&voff_a)[MT],
-                                                 const uint32_t (&voff_b)[Stream<BITS>::kLoads], int chunk,
+                                                 const uint32_t (&voff_b)[Stream<BITS, CT>::kLoads], int chunk,
                                                  int a_stride) {
   const int soff_a = chunk * a_stride;
-  const int soff_b = chunk * Stream<BITS>::kChunkBytes;
+  const int soff_b = chunk * Stream<BITS, CT>::kFullChunkBytes;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
     st.a[mt] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, (int)voff_a[mt], soff_a, 0));
 #pragma unroll
-  for (int l = 0; l < Stream<BITS>::kLoads; ++l)
+  for (int l = 0; l < Stream<BITS, CT>::kLoads; ++l)
     st.b[l] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, (int)voff_b[l], soff_b, kStreamOnce));
 }
 
 // Copy a stage's weight bytes into LDS slot `slot` (byte address).
-template <int BITS, int MT>
-__device__ __forceinline__ void stage_to_lds(const ChainStage<BITS, MT> &st, char *slot,
-                                             const uint32_t (&wr_off)[Stream<BITS>::kLoads],
-                                             const uint32_t (&wrap_off)[Stream<BITS>::kLoads]) {
+template <int BITS, int MT, int CT = 8>
+__device__ __forceinline__ void stage_to_lds(const ChainStage<BITS, MT, CT> &st, char *slot,
+                                             const uint32_t (&wr_off)[Stream<BITS, CT>::kLoads],
+                                             const uint32_t (&wrap_off)[Stream<BITS, CT>::kLoads]) {
 #pragma unroll
-  for (int l = 0; l < Stream<BITS>::kLoads; ++l) {
+  for (int l = 0; l < Stream<BITS, CT>::kLoads; ++l) {
     *(u32x4 *)(slot + wr_off[l]) = st.b[l];
     *(uint32_t *)(slot + wrap_off[l]) = st.b[l][0];
   }
 }
 
-// The lane's words of a staged chunk: 2 or 3 dwords of each of the 8 tiles.
-// All 8 reads are issued together so that their LDS latencies overlap.
-template <int BITS>
+// The lane's words of a staged chunk: 2 or 3 dwords of each of the CT tiles.
+// All CT reads are issued together so that their LDS latencies overlap.
+template <int BITS, int CT = 8>
 __device__ __forceinline__ void read_chain_chunk(const char *slot, uint32_t rd_off,
-                                                 uint32_t (&w)[8][BitsTraits<BITS>::kDwords]) {
+                                                 uint32_t (&w)[CT][BitsTraits<BITS>::kDwords]) {
 #pragma unroll
-  for (int t = 0; t < 8; ++t) {
-    const uint32_t *q = (const uint32_t *)(slot + rd_off + t * Stream<BITS>::kStride);
+  for (int t = 0; t < CT; ++t) {
+    const uint32_t *q = (const uint32_t *)(slot + rd_off + t * Stream<BITS, CT>::kStride);
 #pragma unroll
     for (int d = 0; d < BitsTraits<BITS>::kDwords; ++d) w[t][d] = q[d];
   }
 }
 
-template <int BITS, int MT>
-__device__ __forceinline__ void decode_chain_chunk(const uint32_t (&w)[8][BitsTraits<BITS>::kDwords],
-                                                   const ChainStage<BITS, MT> &st, uint32_t shift, const CbConst &cb,
-                                                   f32x4 (&acc)[MT][8]) {
+template <int BITS, int MT, int CT = 8>
+__device__ __forceinline__ void decode_chain_chunk(const uint32_t (&w)[CT][BitsTraits<BITS>::kDwords],
+                                                   const ChainStage<BITS, MT, CT> &st, uint32_t shift,
+                                                   const CbConst &cb, f32x4 (&acc)[MT][CT]) {
 #pragma unroll
-  for (int t = 0; t < 8; ++t) {
+  for (int t = 0; t < CT; ++t) {
     const half8 bf = decode8<BITS>(w[t], shift, cb);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
@@ -815,21 +818,22 @@ __device__ __forceinline__ float *partial_frag(const MemberArgs &m, int s, int r
 // Per-wave constants of the chain loop: buffer resources, lane offsets of
 // the A loads, the 128-bit B loads and their LDS slots, and the lane's read
 // offset and bit shift in a staged chunk.
-template <int BITS, int MT>
+template <int BITS, int MT, int CT = 8>
 struct ChainCtx {
   __amdgpu_buffer_rsrc_t ra, rb;
   uint32_t voff_a[MT];
   int a_stride;                     // bytes from one chunk of Xr to the next (chunk-major: 64 M)
-  uint32_t voff_b[Stream<BITS>::kLoads], wr_off[Stream<BITS>::kLoads], wrap_off[Stream<BITS>::kLoads];
+  uint32_t voff_b[Stream<BITS, CT>::kLoads], wr_off[Stream<BITS, CT>::kLoads], wrap_off[Stream<BITS, CT>::kLoads];
   uint32_t rd_off, shift;
   CbConst cb;
 };
 
-template <int BITS, int MT>
-__device__ __forceinline__ ChainCtx<BITS, MT> chain_ctx(const MemberArgs &m, int M, int K, int nb, int row_base,
-                                                       int lane, bool chunk_major) {
-  using SB = Stream<BITS>;
-  ChainCtx<BITS, MT> x;
+// `half`: which CT column tiles of the block's 8 the wave streams (CT = 4).
+template <int BITS, int MT, int CT = 8>
+__device__ __forceinline__ ChainCtx<BITS, MT, CT> chain_ctx(const MemberArgs &m, int M, int K, int nb, int row_base,
+                                                           int lane, bool chunk_major, int half = 0) {
+  using SB = Stream<BITS, CT>;
+  ChainCtx<BITS, MT, CT> x;
   x.ra = make_rsrc(m.xr, (uint32_t)((uint64_t)M * K * 2));
   x.rb = make_rsrc(m.words + (int64_t)nb * m.block_stride, (uint32_t)(16u * K * BITS));
   const int c = lane & 15, g = lane >> 4;
@@ -841,21 +845,26 @@ __device__ __forceinline__ ChainCtx<BITS, MT> chain_ctx(const MemberArgs &m, int
     const int row = row_base + 16 * mt + c;
     x.voff_a[mt] = row < M ? (uint32_t)(row * (chunk_major ? 64 : 2 * K) + 16 * g) : kOutOfRange;
   }
-  // 128-bit load l covers chunk bytes [1024 l, 1024 l + 1024); lane bytes
-  // 16 lane .. +15 of it belong to one tile (tiles are 32b bytes, a multiple
-  // of 16). Lanes past the chunk's end load its first bytes and dump them.
+  // 128-bit load l covers bytes [1024 l, 1024 l + 1024) of the wave's part
+  // of a chunk: CT tiles of tile row 0, then CT of tile row 1 (in memory the
+  // chunk is tile row 0's 8 tiles, then tile row 1's; the wave's tiles start
+  // at tile CT * half of each). Lane bytes 16 lane .. +15 of a load belong to
+  // one tile (tiles are 32b bytes, a multiple of 16), staged as tile tau of
+  // the wave's 2 CT. Lanes past the end load the chunk's first bytes and dump
+  // them.
 #pragma unroll
   for (int l = 0; l < SB::kLoads; ++l) {
     const int off = 1024 * l + 16 * lane;
     const bool valid = off < SB::kChunkBytes;
-    const int tau = off / (32 * BITS), w = off % (32 * BITS);
-    x.voff_b[l] = valid ? (uint32_t)off : 0u;
-    x.wr_off[l] = valid ? (uint32_t)(tau * SB::kStride + w) : (uint32_t)(16 * SB::kStride);
-    x.wrap_off[l] = valid ? (uint32_t)(tau * SB::kStride + 32 * BITS + (w == 0 ? 0 : 4)) : (uint32_t)(16 * SB::kStride);
+    const int row = off / (CT * 32 * BITS), within = off % (CT * 32 * BITS);
+    const int tau = row * CT + within / (32 * BITS), w = within % (32 * BITS);
+    x.voff_b[l] = valid ? (uint32_t)(row * 256 * BITS + half * CT * 32 * BITS + within) : 0u;
+    x.wr_off[l] = valid ? (uint32_t)(tau * SB::kStride + w) : (uint32_t)(2 * CT * SB::kStride);
+    x.wrap_off[l] = valid ? (uint32_t)(tau * SB::kStride + 32 * BITS + (w == 0 ? 0 : 4)) : (uint32_t)(2 * CT * SB::kStride);
   }
   const int jseg = 2 * c + (g & 1);
   x.shift = 8u * (uint32_t)((BITS * jseg) & 3);
-  x.rd_off = (uint32_t)((g >> 1) * 8 * SB::kStride + 4 * ((BITS * jseg) >> 2));
+  x.rd_off = (uint32_t)((g >> 1) * CT * SB::kStride + 4 * ((BITS * jseg) >> 2));
   x.cb = cb_const();
   return x;
 }
@@ -871,25 +880,25 @@ struct NoWait {
 // region `wlds`; the next chunk is copied to LDS before chunk i is decoded.
 // With `fused` the first P chunks' weight loads go out before ready(), which
 // returns once the chain's part of Xr is written, and their Xr loads after.
-template <int BITS, int MT, int P, typename Ready = NoWait>
-__device__ __forceinline__ void run_chain(f32x4 (&acc)[MT][8], int c0, int c1, char *wlds,
-                                          const ChainCtx<BITS, MT> &x, bool fused = false, Ready ready = Ready{}) {
-  using SB = Stream<BITS>;
+template <int BITS, int MT, int P, int CT = 8, typename Ready = NoWait>
+__device__ __forceinline__ void run_chain(f32x4 (&acc)[MT][CT], int c0, int c1, char *wlds,
+                                          const ChainCtx<BITS, MT, CT> &x, bool fused = false, Ready ready = Ready{}) {
+  using SB = Stream<BITS, CT>;
   static_assert(P % 2 == 0, "the chunk loop unrolls by P, a multiple of the 2 LDS slots");
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int t = 0; t < 8; ++t) acc[mt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < CT; ++t) acc[mt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int n = c1 - c0;
   const int last = c1 - 1;
-  ChainStage<BITS, MT> st[P];
+  ChainStage<BITS, MT, CT> st[P];
   if (fused) {
 #pragma unroll
     for (int p = 0; p < P; ++p)
 #pragma unroll
       for (int l = 0; l < SB::kLoads; ++l)
         st[p].b[l] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                   x.rb, (int)x.voff_b[l], min(c0 + p, last) * SB::kChunkBytes,
+                                                   x.rb, (int)x.voff_b[l], min(c0 + p, last) * SB::kFullChunkBytes,
                                                    kStreamOnce));
     __builtin_amdgcn_sched_barrier(0);
     ready();
@@ -904,23 +913,23 @@ __device__ __forceinline__ void run_chain(f32x4 (&acc)[MT][8], int c0, int c1, c
   } else {
 #pragma unroll
     for (int p = 0; p < P; ++p) {
-      load_chain_stage<BITS, MT>(st[p], x.ra, x.rb, x.voff_a, x.voff_b, min(c0 + p, last), x.a_stride);
+      load_chain_stage<BITS, MT, CT>(st[p], x.ra, x.rb, x.voff_a, x.voff_b, min(c0 + p, last), x.a_stride);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
-  stage_to_lds<BITS, MT>(st[0], wlds, x.wr_off, x.wrap_off);
+  stage_to_lds<BITS, MT, CT>(st[0], wlds, x.wr_off, x.wrap_off);
   // per chunk: read the staged chunk's words, stage the next chunk into the
   // other slot, decode and multiply, refill the register stage
-  uint32_t w[8][BitsTraits<BITS>::kDwords];
+  uint32_t w[CT][BitsTraits<BITS>::kDwords];
   int i = 0;
   for (; i + P < n; i += P) {
 #pragma unroll
     for (int p = 0; p < P; ++p) {
-      read_chain_chunk<BITS>(wlds + (p % 2) * SB::kSlot, x.rd_off, w);
+      read_chain_chunk<BITS, CT>(wlds + (p % 2) * SB::kSlot, x.rd_off, w);
       __builtin_amdgcn_sched_barrier(0);
-      stage_to_lds<BITS, MT>(st[(p + 1) % P], wlds + ((p + 1) % 2) * SB::kSlot, x.wr_off, x.wrap_off);
-      decode_chain_chunk<BITS, MT>(w, st[p], x.shift, x.cb, acc);
-      load_chain_stage<BITS, MT>(st[p], x.ra, x.rb, x.voff_a, x.voff_b, min(c0 + i + p + P, last), x.a_stride);
+      stage_to_lds<BITS, MT, CT>(st[(p + 1) % P], wlds + ((p + 1) % 2) * SB::kSlot, x.wr_off, x.wrap_off);
+      decode_chain_chunk<BITS, MT, CT>(w, st[p], x.shift, x.cb, acc);
+      load_chain_stage<BITS, MT, CT>(st[p], x.ra, x.rb, x.voff_a, x.voff_b, min(c0 + i + p + P, last), x.a_stride);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -929,9 +938,9 @@ __device__ __forceinline__ void run_chain(f32x4 (&acc)[MT][8], int c0, int c1, c
 #pragma unroll
   for (int p = 0; p < P; ++p) {
     if (p < r) {
-      read_chain_chunk<BITS>(wlds + (p % 2) * SB::kSlot, x.rd_off, w);
-      if (p + 1 < r) stage_to_lds<BITS, MT>(st[(p + 1) % P], wlds + ((p + 1) % 2) * SB::kSlot, x.wr_off, x.wrap_off);
-      decode_chain_chunk<BITS, MT>(w, st[p], x.shift, x.cb, acc);
+      read_chain_chunk<BITS, CT>(wlds + (p % 2) * SB::kSlot, x.rd_off, w);
+      if (p + 1 < r) stage_to_lds<BITS, MT, CT>(st[(p + 1) % P], wlds + ((p + 1) % 2) * SB::kSlot, x.wr_off, x.wrap_off);
+      decode_chain_chunk<BITS, MT, CT>(w, st[p], x.shift, x.cb, acc);
     }
   }
 }
@@ -1113,10 +1122,15 @@ void linear_spread_kernel(const LinearArgs a) {
 // ------------------------------------------------------------ linear, 16 and 32 rows per workgroup
 
 // W = 8 (chained, 16 rows) keeps to 128 VGPRs so that two workgroups fit a CU.
-template <int BITS, int MT, bool CHAINED, int W>
+// CT = 4 (exchanged, 16 rows, W = 8): the two waves 2i, 2i+1 share split i of
+// the workgroup, each with 4 of the block's 8 column tiles: the same MFMA
+// chains, two waves per SIMD where one wave per split would leave one.
+template <int BITS, int MT, bool CHAINED, int W, int CT = 8>
 __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(W == 8 ? 4 : 1)))
 void linear_chain_kernel(const LinearArgs a) {
-  using SB = Stream<BITS>;
+  static_assert(CT == 8 || (CT == 4 && !CHAINED && MT == 1), "column halves: exchanged 16-row tiles only");
+  using SB = Stream<BITS, CT>;
+  constexpr int SPW = W * CT / 8;                        // splits per workgroup and round
   constexpr int R = 16 * MT;
   constexpr int NT = W * 64;                             // threads
   const int lane = threadIdx.x & 63;
@@ -1149,28 +1163,30 @@ void linear_chain_kernel(const LinearArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[kLds];
   char *wlds = lds + wave * SB::kWave;
 
-  const ChainCtx<BITS, MT> x = chain_ctx<BITS, MT>(m, M, K, nb, row_base, lane, false);
+  const int sw = wave / (8 / CT), half = wave % (8 / CT);   // the wave's split in the workgroup, its columns
+  const ChainCtx<BITS, MT, CT> x = chain_ctx<BITS, MT, CT>(m, M, K, nb, row_base, lane, false, half);
   const int c = lane & 15, g = lane >> 4;
-  // one row block (row_base == 0); the 8-wave form (weights of many blocks,
-  // where a rotation launch costs little) would spill with the fused prologue
-  const bool fused = W != 8 && a.x != nullptr;
+  // one row block (row_base == 0); the 8-wave chained form (weights of many
+  // blocks, where a rotation launch costs little) would spill with the fused
+  // prologue
+  const bool fused = (W != 8 || CT == 4) && a.x != nullptr;
   __shared__ int s_clear;
   if (fused) rot_produce<4 * MT>(a, wave, lane, false);
 
-  const int s_first = CHAINED ? wave : W * sg + wave;
-  const int rounds = CHAINED ? (S + W - 1) / W : 1;
+  const int s_first = CHAINED ? sw : SPW * sg + sw;
+  const int rounds = CHAINED ? (S + SPW - 1) / SPW : 1;
   float zsum[CHAINED ? R * kBlockCols / NT : 1];
 
   for (int round = 0; round < rounds; ++round) {
-    const int s = s_first + round * (CHAINED ? W : 0);
+    const int s = s_first + round * (CHAINED ? SPW : 0);
     const bool active = s < S;                           // uniform per wave
-    f32x4 acc[MT][8];
+    f32x4 acc[MT][CT];
     if (CHAINED && round > 0) __syncthreads();           // fold buffers of the last round are read
     if (active) {
       // in 128 VGPRs (W = 8) only 2 chunks of more than two 128-bit loads fit
       constexpr int P = (W == 8 && SB::kLoads > 2) ? 2 : ChainDepth<MT>::P;
       const int c0 = (int)(((int64_t)s * C) / S), c1 = (int)(((int64_t)(s + 1) * C) / S);
-      run_chain<BITS, MT, P>(acc, c0, c1, wlds, x, fused,
+      run_chain<BITS, MT, P, CT>(acc, c0, c1, wlds, x, fused,
                              [&] { rot_wait<4 * MT>(a, j, c0 >> 2, (c1 - 1) >> 2, lane, false); });
     }
     if constexpr (CHAINED) {
@@ -1205,10 +1221,10 @@ void linear_chain_kernel(const LinearArgs a) {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-          for (int t = 0; t < 8; ++t)
+          for (int t = 0; t < CT; ++t)
             if (row_base + 16 * mt + 4 * g < M)
               __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[mt][t]), rp,
-                                                     (mt * 8 + t) * 1024 + 16 * lane, 0, kAgentScope);
+                                                     (mt * 8 + half * CT + t) * 1024 + 16 * lane, 0, kAgentScope);
       }
     }
   }
@@ -2317,6 +2333,7 @@ template <int BITS>
 LinearFn pick_linear(int kernel, bool chained) {
   if (kernel == kSpread16) return linear_spread_kernel<BITS>;
   if (kernel == kChain16x8) return linear_chain_kernel<BITS, 1, true, 8>;
+  if (kernel == kChain16H) return linear_chain_kernel<BITS, 1, false, 8, 4>;
   if (kernel == kWide128) return linear_wide_kernel<BITS>;
   if (kernel == kBlock128) return chained ? linear_block_kernel<BITS, true> : linear_block_kernel<BITS, false>;
   if (kernel == kQuad128) return linear_quad_kernel<BITS>;
@@ -2326,8 +2343,9 @@ LinearFn pick_linear(int kernel, bool chained) {
 }  // namespace
 
 int launch_linear(const LinearArgs &a, int bits, int kernel, bool chained, void *stream) {
-  if (kernel < kChain16 || kernel > kQuad128 ||
-      ((kernel == kChain16x8 || kernel == kSpread16 || kernel == kWide128 || kernel == kQuad128) && !chained))
+  if (kernel < kChain16 || kernel > kChain16H ||
+      ((kernel == kChain16x8 || kernel == kSpread16 || kernel == kWide128 || kernel == kQuad128) && !chained) ||
+      (kernel == kChain16H && chained))
     return (int)hipErrorInvalidValue;
   LinearFn fn = nullptr;
   switch (bits) {
