@@ -282,10 +282,12 @@ def test_rotate_and_linear_rotated_are_one_launch_each(lib):
 
 def test_rotation_runs_inside_the_linear_launch_up_to_32_rows(lib):
     """Launch-gap removal (PR #1467, "What this changes": the rotations and
-    decode-row linears chained without a gap), opt-in: with it on, a call of
-    up to 32 rows is one launch and above that two; off (the default), two
-    everywhere. The counter region holds the chunk flags either way (one word
-    per member and 128 columns of K, plus a count)."""
+    decode-row linears chained without a gap), opt-in: with it on, a call
+    whose launch is one row block of at most 32 rows (the 16-row forms; the
+    32-row tiling, here forced at 17..32 rows, where the automatic choice
+    takes two 16-row blocks) is one launch and everything else two; off (the
+    default), two everywhere. The counter region holds the chunk flags either
+    way (one word per member and 128 columns of K, plus a count)."""
     ex.exl3_test_mock(True)
     a = fake_weight(5120, 6144, 4)
     b = fake_weight(5120, 1024, 4, base=0x50000000)
@@ -303,10 +305,14 @@ def test_rotation_runs_inside_the_linear_launch_up_to_32_rows(lib):
         assert launches(M) == 2, M
     ex.exl3_test_fuse_rotation(True)
     try:
-        for M in (1, 7, 16, 17, 32):
+        for M in (1, 7, 16):
             assert launches(M) == 1, M
-        for M in (33, 64, 128, 300):
+        for M in (17, 32, 33, 64, 128, 300):
             assert launches(M) == 2, M
+        ex.exl3_test_force(2, -1, 0)
+        for M in (17, 32):
+            assert launches(M) == 1, M
+        ex.exl3_test_force(-1, -1, 0)
         # the two-phase calls never fuse
         assert lib.exl3_rotate(3, arr, 0x30000000, 5120, 16, ctypes.byref(ws), None) == 0
         assert lib.exl3_linear_rotated(3, arr, 16, ys, ld, ctypes.byref(ws), None) == 0

@@ -122,21 +122,55 @@ int cu_count() {
 // several rounds without partials.
 constexpr int64_t kChainedMinBlocks16 = 512;
 
+// Mid-M rows (17..128) with the automatic tiling: the row tiling and
+// whether the splits of a block fold inside one workgroup (chained) or
+// exchange through the workspace, chosen from measurements on MI355X of the
+// 27B's weights (gate/up at 3 bits, q/k/v, down, a 5120 x 8192 weight and
+// the 6-bit head at 17..128 rows; every choice gives the same bits). The
+// 8-wave chained 16-row form over ceil(M / 16) row blocks is the fastest
+// wherever its workgroups fill the chip without too many rounds; the 64-row
+// tiling never was.
+struct MidChoice {
+  int m_tiles;
+  bool chained;
+};
+
+MidChoice mid_m_choice(int64_t blocks, bool long_chains, int64_t M) {
+  const int64_t w16 = blocks * ((M + 15) / 16);            // workgroups of the chained 16-row form
+  if (blocks >= 128) return w16 <= 1024 ? MidChoice{1, true} : MidChoice{8, true};
+  if (!long_chains) return M <= 32 ? MidChoice{1, false} : MidChoice{1, true};
+  // few blocks, long splits (down): the exchange keeps the CUs busy
+  if (M <= 32) return {2, false};
+  if (M <= 48) return {1, false};
+  if (M <= 96) return {1, true};
+  return {8, false};
+}
+
 Launch choose_launch(const MemberPlan *mp, int n, int64_t M) {
   Launch L;
-  int mt = g_hooks.m_tiles;
-  // 16: 128-row tiles two blocks wide; automatic above 128 rows
-  const bool wide = mt == 16 || (mt == -1 && M > 128);
-  if (mt == 16) mt = 8;
-  else if (mt != 1 && mt != 2 && mt != 4 && mt != 8) mt = M <= 16 ? 1 : M <= 32 ? 2 : M <= 64 ? 4 : 8;
-  L.m_tiles = mt;
-  L.row_blocks = (M + 16 * mt - 1) / (16 * mt);
   bool all_single = true;
   int64_t blocks = 0;
+  bool long_chains = false;
   for (int j = 0; j < n; ++j) {
     all_single = all_single && mp[j].splits == 1;
     blocks += mp[j].n_blocks;
+    long_chains = long_chains || (mp[j].w->K / kChunk) > 16 * mp[j].splits;
   }
+  int mt = g_hooks.m_tiles;
+  // 16: 128-row tiles two blocks wide; automatic above 128 rows
+  const bool wide = mt == 16 || (mt == -1 && M > 128);
+  int mid_chained = -1;
+  if (mt == 16) {
+    mt = 8;
+  } else if (mt == -1 && M > 16 && M <= 128) {
+    const MidChoice mc = mid_m_choice(blocks, long_chains, M);
+    mt = mc.m_tiles;
+    mid_chained = mc.chained ? 1 : 0;
+  } else if (mt != 1 && mt != 2 && mt != 4 && mt != 8) {
+    mt = M <= 16 ? 1 : 8;
+  }
+  L.m_tiles = mt;
+  L.row_blocks = (M + 16 * mt - 1) / (16 * mt);
   // one plan S <= 15 for every member and one 16-row block: the spread
   // launch is possible
   int32_t s_uniform = mp[0].splits;
@@ -154,6 +188,8 @@ Launch choose_launch(const MemberPlan *mp, int n, int64_t M) {
       L.left_blocks = blocks * (16 - s_uniform) / 16;
       L.own_blocks = blocks - L.left_blocks;
     }
+  } else if (mid_chained >= 0) {
+    L.chained = mid_chained == 1 || all_single;
   } else if (mt == 1) {
     if (all_single || blocks >= kChainedMinBlocks16) {
       L.chained = true;
@@ -181,8 +217,6 @@ Launch choose_launch(const MemberPlan *mp, int n, int64_t M) {
   // 128-row tiles: the block tiling (4 waves of 128 x 32, operands copied
   // into an LDS ring), except exchanged splits of more than 16 chunks, which
   // run faster on the 2 x 2 tiling
-  bool long_chains = false;
-  for (int j = 0; j < n; ++j) long_chains = long_chains || (mp[j].w->K / kChunk) > 16 * mp[j].splits;
   const bool quad = g_prompt_mode == 1 && M > 128 && g_hooks.m_tiles == -1 && g_hooks.chained != 0;
   // 16-row exchanged launches of at most one split chain per SIMD run each
   // chain on two waves (4 column tiles each): a lone wave per SIMD leaves
@@ -306,12 +340,14 @@ int exl3_workspace_need(int32_t n_members, const exl3_weight_t *const *w, int64_
   const int e = check_group(n_members, w, M, mp);
   if (e != EXL3_OK) return e;
   size_t rest = 0, cb = 0;
-  // sizes grow with M inside each regime; the regime boundaries (16 and 32
-  // rows: the 16- and 32-row tilings, which also hold the rotation flags;
-  // 128: the mid-M tilings) and M itself bound every smaller call. The
-  // counter region sits at a fixed offset, so the largest counter need and
-  // the largest rest add up.
-  const int64_t probes[4] = {std::min<int64_t>(M, 16), std::min<int64_t>(M, 32), std::min<int64_t>(M, 128), M};
+  // sizes grow with M while the launch form stays the same; the row counts
+  // where the automatic choice changes form (16, 32, 48, 96 and 128 rows; the
+  // 16- and 32-row forms also hold the rotation flags) and M itself bound
+  // every smaller call. The counter region sits at a fixed offset, so the
+  // largest counter need and the largest rest add up.
+  const int64_t bounds[6] = {16, 32, 48, 96, 128, M};
+  int64_t probes[6];
+  for (int i = 0; i < 6; ++i) probes[i] = std::min<int64_t>(M, bounds[i]);
   for (int64_t p : probes)
     if (p > 0) call_need(mp, n_members, p, &rest, &cb);
   *counter_bytes = cb;
