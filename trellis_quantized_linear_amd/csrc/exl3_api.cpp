@@ -452,8 +452,18 @@ int run_group(int32_t n_members, const exl3_weight_t *const *w, const void *x, i
   ra.K = (int32_t)K;
   ra.n_members = n_members;
   ra.natural_order = 0;
-  // the spread launch reads Xr chunk-major, every other launch row-major
-  ra.chunk_major = L.kernel == exl3::kSpread16 ? 1 : 0;
+  // Xr layout. Row-major rows lie 2K bytes apart, so the 128 rows of one
+  // chunk that every workgroup of a 128-row tiling loads at about the same
+  // time fall on few memory channels; chunk-major puts them in one
+  // contiguous 8 KB (the 3-bit {gate, up} pair at 128 rows: 121 -> 100 us).
+  // The spread launch reads chunk-major too (its 16 rows as 8 whole lines);
+  // the other 16- to 64-row launches measured as fast or faster row-major.
+  // Chunk offsets are 32-bit: chunk-major needs 2 K M < 2^31.
+  const bool tile_cm = (L.kernel == exl3::kTile128 || L.kernel == exl3::kBlock128 || L.kernel == exl3::kWide128 ||
+                        L.kernel == exl3::kQuad128) &&
+                       2 * K * M < (int64_t(1) << 31);
+  ra.chunk_major = L.kernel == exl3::kSpread16 || tile_cm ? 1 : 0;
+  la.xr_chunk_major = tile_cm ? 1 : 0;
   la.n_members = n_members;
   la.M = (int32_t)M;
   la.K = (int32_t)K;

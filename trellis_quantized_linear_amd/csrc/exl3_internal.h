@@ -19,7 +19,7 @@ struct MemberArgs {
   const uint16_t *scales;     // fp16[N]
   const uint16_t *svh;        // fp16[N]
   const uint16_t *xr;         // rotated input, fp16, slot order: [M][K], or [K/32][M][32] (chunk-major)
-                              // for the spread launch
+                              // for the spread launch and the 128-row tilings (LinearArgs::xr_chunk_major)
   const uint16_t *suh;        // fp16[K] input signs (read when the rotation is fused)
   uint16_t *y;                // bf16 [M][ldy]
   float *partials;            // [S][M][N] fp32, or null when chained
@@ -44,6 +44,7 @@ struct LinearArgs {
   int32_t total_wgs;
   int32_t own_blocks;         // spread launch: blocks owned by one workgroup each (= total_wgs)
   int32_t left_blocks;        // spread launch: blocks whose splits go to spare waves
+  int32_t xr_chunk_major;     // 128-row tilings: Xr is chunk-major (else row-major)
   // Fused input rotation (decode and 32-row launches): the launch itself
   // writes every member's Xr from x before its chains read it. sync[0]
   // counts finished workgroups; sync[1 + j * K/128 + k] says that member j's

@@ -1325,10 +1325,10 @@ struct TileStage {
 };
 
 __device__ __forceinline__ void load_tile_stage(TileStage &st, __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
-                                                const uint32_t (&voff_a)[2], uint32_t voff_b, int chunk,
+                                                const uint32_t (&voff_a)[2], int a_step, uint32_t voff_b, int chunk,
                                                 int chunk_bytes) {
-  st.a[0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, (int)voff_a[0], chunk * 64, 0));
-  st.a[1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, (int)voff_a[1], chunk * 64, 0));
+  st.a[0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, (int)voff_a[0], chunk * a_step, 0));
+  st.a[1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, (int)voff_a[1], chunk * a_step, 0));
   st.b = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, (int)voff_b, chunk * chunk_bytes, 0));
 }
 
@@ -1395,7 +1395,10 @@ void linear_tile_kernel(const LinearArgs a) {
   constexpr int kEpi = 64 * 132 * 4;
   __shared__ __attribute__((aligned(16))) char lds[kStage > kEpi ? kStage : kEpi];
 
+  // Xr row-major or chunk-major (each chunk's M rows contiguous, 64 bytes a row)
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(m.xr, (uint32_t)((uint64_t)M * K * 2));
+  const bool cm = a.xr_chunk_major != 0;
+  const int a_step = cm ? 64 * M : 64;                       // bytes from one chunk to the next
   const __amdgpu_buffer_rsrc_t rbuf = make_rsrc(m.words + (int64_t)nb * m.block_stride, (uint32_t)(16u * K * BITS));
   const int c = lane & 15, g = lane >> 4;
 
@@ -1407,7 +1410,7 @@ void linear_tile_kernel(const LinearArgs a) {
   for (int i = 0; i < 2; ++i) {
     const int r = 32 * wave + 16 * i + (lane >> 2);
     const int row = row_base + r;
-    voff_a[i] = row < M ? (uint32_t)(row * 2 * K + 16 * (lane & 3)) : kOutOfRange;
+    voff_a[i] = row < M ? (uint32_t)(row * (cm ? 64 : 2 * K) + 16 * (lane & 3)) : kOutOfRange;
     a_wr[i] = (uint32_t)(r * TL::kArow + 16 * (lane & 3));
   }
   const int boff = 1024 * wave + 16 * lane;
@@ -1445,7 +1448,7 @@ void linear_tile_kernel(const LinearArgs a) {
   TileStage st[P];
 #pragma unroll
   for (int p = 0; p < P; ++p) {
-    load_tile_stage(st[p], ra, rbuf, voff_a, voff_b, min(cb + p, last), SB::kChunkBytes);
+    load_tile_stage(st[p], ra, rbuf, voff_a, a_step, voff_b, min(cb + p, last), SB::kChunkBytes);
     __builtin_amdgcn_sched_barrier(0);
   }
   tile_stage_to_lds<BITS>(st[0], lds, a_wr, b_wr, b_wrap);
@@ -1455,7 +1458,7 @@ void linear_tile_kernel(const LinearArgs a) {
   auto step = [&](int cc, char *cur, char *nxt, TileStage &mine, TileStage &next, bool has_next) {
     __syncthreads();
     if (has_next) tile_stage_to_lds<BITS>(next, nxt, a_wr, b_wr, b_wrap);
-    load_tile_stage(mine, ra, rbuf, voff_a, voff_b, min(cc + P, last), SB::kChunkBytes);
+    load_tile_stage(mine, ra, rbuf, voff_a, a_step, voff_b, min(cc + P, last), SB::kChunkBytes);
     compute_tile_chunk<BITS>(cur, a_rd, b_rd, shift, cbc, acc);
     if (cc + 1 == bnd) {                                   // chain s complete (uniform)
       if constexpr (CHAINED) {
@@ -1665,12 +1668,16 @@ void linear_wide_kernel(const LinearArgs a) {
   // 16 (2w + e) + l % 16, 16-byte column l / 16) and tile row slot w (block
   // w / 2, tile row w % 2) of every chunk
   const __amdgpu_buffer_rsrc_t ra =
-      make_rsrc(m.xr + (int64_t)row_base * K, (uint32_t)min(M - row_base, 128) * (uint32_t)K * 2u);
+      a.xr_chunk_major ? make_rsrc(m.xr + (int64_t)row_base * kChunk, (uint32_t)(C * M - row_base) * 64u)
+                       : make_rsrc(m.xr + (int64_t)row_base * K, (uint32_t)min(M - row_base, 128) * (uint32_t)K * 2u);
+  // Xr chunk-major (each chunk's M rows contiguous, 64 bytes a row) or row-major
+  const int a_row = a.xr_chunk_major ? 64 : 2 * K;           // bytes from one row to the next
+  const int a_step = a.xr_chunk_major ? 64 * M : 64;         // bytes from one chunk to the next
   uint32_t va[2];
 #pragma unroll
   for (int e = 0; e < 2; ++e) {
     const int r = 16 * (2 * wave + e) + c;                   // operand 2w + e: rows 16 (2w + e) + l % 16
-    va[e] = row_base + r < M ? (uint32_t)(r * 2 * K + 16 * g) : kOutOfRange;
+    va[e] = row_base + r < M ? (uint32_t)(r * a_row + 16 * g) : kOutOfRange;
   }
   const __amdgpu_buffer_rsrc_t rw =
       make_rsrc(m.words + (int64_t)2 * pair * m.block_stride, (uint32_t)(n_blk * m.block_stride));
@@ -1683,7 +1690,7 @@ void linear_wide_kernel(const LinearArgs a) {
   }
   auto issue_copies = [&](int chunk, char *stage) {
 #pragma unroll
-    for (int e = 0; e < 2; ++e) copy_to_lds(ra, stage + 1024 * (2 * wave + e), va[e], chunk * 64);
+    for (int e = 0; e < 2; ++e) copy_to_lds(ra, stage + 1024 * (2 * wave + e), va[e], chunk * a_step);
 #pragma unroll
     for (int e = 0; e < WL::kRowCopies; ++e)
       copy_to_lds(rw, stage + WL::kA + wave * WL::kRow + 1024 * e, vw[e], chunk * 512 * BITS);
@@ -1897,12 +1904,16 @@ void linear_block_kernel(const LinearArgs a) {
   // 16 (2w + e) + l % 16, 16-byte column l / 16) and half w % 2 of tile row
   // w / 2 of every chunk
   const __amdgpu_buffer_rsrc_t ra =
-      make_rsrc(m.xr + (int64_t)row_base * K, (uint32_t)min(M - row_base, 128) * (uint32_t)K * 2u);
+      a.xr_chunk_major ? make_rsrc(m.xr + (int64_t)row_base * kChunk, (uint32_t)(C * M - row_base) * 64u)
+                       : make_rsrc(m.xr + (int64_t)row_base * K, (uint32_t)min(M - row_base, 128) * (uint32_t)K * 2u);
+  // Xr chunk-major (each chunk's M rows contiguous, 64 bytes a row) or row-major
+  const int a_row = a.xr_chunk_major ? 64 : 2 * K;           // bytes from one row to the next
+  const int a_step = a.xr_chunk_major ? 64 * M : 64;         // bytes from one chunk to the next
   uint32_t va[2];
 #pragma unroll
   for (int e = 0; e < 2; ++e) {
     const int r = 16 * (2 * wave + e) + c;
-    va[e] = row_base + r < M ? (uint32_t)(r * 2 * K + 16 * g) : kOutOfRange;
+    va[e] = row_base + r < M ? (uint32_t)(r * a_row + 16 * g) : kOutOfRange;
   }
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(m.words + (int64_t)nb * m.block_stride, (uint32_t)m.block_stride);
   const int hrow = wave >> 1, half = wave & 1;
@@ -1911,7 +1922,7 @@ void linear_block_kernel(const LinearArgs a) {
   auto stage_of = [&](int i) { return lds + (int)((unsigned)i % NS) * BL::kStage; };
   auto issue_copies = [&](int chunk, char *stage) {
 #pragma unroll
-    for (int e = 0; e < 2; ++e) copy_to_lds(ra, stage + 1024 * (2 * wave + e), va[e], chunk * 64);
+    for (int e = 0; e < 2; ++e) copy_to_lds(ra, stage + 1024 * (2 * wave + e), va[e], chunk * a_step);
     copy_to_lds(rw, stage + BL::kA + hrow * BL::kRow + half * 1024, vw, chunk * 512 * BITS);
   };
 
@@ -2159,12 +2170,16 @@ void linear_quad_kernel(const LinearArgs a) {
   // copies: wave w moves input operands 2w + e (lane l: row 16 (2w + e) + l % 16,
   // 16-byte column l / 16) and both tile rows of block w
   const __amdgpu_buffer_rsrc_t ra =
-      make_rsrc(m.xr + (int64_t)row_base * K, (uint32_t)min(M - row_base, 128) * (uint32_t)K * 2u);
+      a.xr_chunk_major ? make_rsrc(m.xr + (int64_t)row_base * kChunk, (uint32_t)(C * M - row_base) * 64u)
+                       : make_rsrc(m.xr + (int64_t)row_base * K, (uint32_t)min(M - row_base, 128) * (uint32_t)K * 2u);
+  // Xr chunk-major (each chunk's M rows contiguous, 64 bytes a row) or row-major
+  const int a_row = a.xr_chunk_major ? 64 : 2 * K;           // bytes from one row to the next
+  const int a_step = a.xr_chunk_major ? 64 * M : 64;         // bytes from one chunk to the next
   uint32_t va[2];
 #pragma unroll
   for (int e = 0; e < 2; ++e) {
     const int r = 16 * (2 * wave + e) + c;
-    va[e] = row_base + r < M ? (uint32_t)(r * 2 * K + 16 * g) : kOutOfRange;
+    va[e] = row_base + r < M ? (uint32_t)(r * a_row + 16 * g) : kOutOfRange;
   }
   const __amdgpu_buffer_rsrc_t rw =
       make_rsrc(m.words + (int64_t)4 * quad * m.block_stride, (uint32_t)(n_blk * m.block_stride));
@@ -2179,7 +2194,7 @@ void linear_quad_kernel(const LinearArgs a) {
   auto stage_of = [&](int i) { return lds + (int)((unsigned)i % NS) * QL::kStage; };
   auto issue_copies = [&](int chunk, char *stage) {
 #pragma unroll
-    for (int e = 0; e < 2; ++e) copy_to_lds(ra, stage + 1024 * (2 * wave + e), va[e], chunk * 64);
+    for (int e = 0; e < 2; ++e) copy_to_lds(ra, stage + 1024 * (2 * wave + e), va[e], chunk * a_step);
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
