@@ -1994,6 +1994,19 @@ void linear_block_kernel(const LinearArgs a) {
       af[mt] = __builtin_bit_cast(half8, *(const u32x4 *)(nxt + a_rd + 1024 * mt));
       if ((mt & 3) == 3) bn[mt >> 2] = decode8<BITS>(wa[mt >> 2], bl.shift, cbc);
     }
+    if constexpr (CHAINED) {
+      // issue order: the copies, the word reads, then per row tile its two
+      // MFMAs, its next A read and a share of the decode (-5 % chained; the
+      // exchanged form measured slightly slower with it)
+      __builtin_amdgcn_sched_group_barrier(0x020, 3, 0);     // buffer-to-LDS copies
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);     // LDS reads
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // VALU
+      }
+    }
   };
   using First = std::integral_constant<bool, true>;
   using Rest = std::integral_constant<bool, false>;
