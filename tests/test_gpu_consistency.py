@@ -284,3 +284,33 @@ def test_split_exchange_stress():
             assert np.array_equal(G.host_u16(y), ref), rep
     ex().exl3_test_force(-1, -1, 0)
     assert int(ws.counters().abs().sum()) == 0
+
+
+TWO_PHASE = [(1, (-1, -1, 0)), (16, (-1, -1, 0)), (16, (1, 2, 4)), (40, (-1, -1, 0)), (64, (-1, -1, 0)),
+             (100, (-1, -1, 0)), (128, (-1, -1, 0)), (128, (8, 0, 0)), (200, (-1, -1, 0))]
+
+
+@pytest.mark.parametrize("M,force", TWO_PHASE)
+def test_two_phase_calls_equal_the_group_call(M, force):
+    """exl3_rotate then exl3_linear_rotated give the bytes of one
+    exl3_linear_group call: the rotation writes Xr in the layout the linear
+    launch of that row count reads (chunk-major for the spread launch, forced
+    here with 4 splits at 16 rows, and for the 128-row tilings at 100, 128
+    and 200 rows, chained and exchanged; row-major for the other 16- to
+    64-row launches)."""
+    torch = G.torch_mod()
+    K = 5120
+    layers = [G.layer("two-phase", n, K, N, 3) for n, N in (("gate", 2048), ("up", 2048), ("k", 1024))]
+    ws_list = [G.upload(L) for L in layers]
+    xd = G.dev_bf16(G.xbits("two-phase", M, K))
+    ex().exl3_test_force(*force)
+    ws = ex().Workspace().reserve(ws_list, M)
+    one = [G.host_u16(y) for y in G.run_group(ws_list, xd, M=M, ws=ws, tag=f"group call {force}")]
+    ys = [G.empty_y(M, L.N) for L in layers]
+    G.say(f"exl3_rotate + exl3_linear_rotated M={M}")
+    ex().exl3_rotate(ws_list, xd, ws, M=M)
+    ex().exl3_linear_rotated(ws_list, ys, ws, M)
+    torch.cuda.synchronize()
+    for j, y in enumerate(ys):
+        assert np.array_equal(G.host_u16(y), one[j]), (M, j)
+    assert int(ws.counters().abs().sum()) == 0
