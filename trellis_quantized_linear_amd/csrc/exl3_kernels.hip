@@ -355,9 +355,12 @@ __device__ __forceinline__ void epilogue_rows_lds(float *zrows, int pitch, const
 // 128-byte lines per load instead of 16 half-used ones whose other halves its
 // 16 streaming waves per CU evict from the L1 before the next chunk, and the
 // L1's outstanding misses are what the weight stream shares with these loads
-// (-5 % on {gate, up} at 16 rows). With 4 or 8 waves per CU the L1 keeps the
-// row-major lines for the next chunk, and row-major measured as fast or
-// faster there.
+// (-5 % on {gate, up} at 16 rows). The 128-row tilings read chunk-major too:
+// their workgroups all load the same chunk's 128 rows at about the same time,
+// and row-major those rows lie 2K bytes apart, on few memory channels (-18 %
+// on the 3-bit {gate, up} pair at 128 rows). The other 16- to 64-row launches
+// (4 or 8 waves per CU, whose L1 keeps the row-major lines for the next
+// chunk) measured as fast or faster row-major.
 
 // 8 consecutive 16-bit values from p (any 2-byte alignment).
 __device__ __forceinline__ u32x4 load8_u16(const uint16_t *p) {
@@ -1513,30 +1516,27 @@ void linear_tile_kernel(const LinearArgs a) {
     __syncthreads();
     if (!s_last) return;
     if (threadIdx.x == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    // z = P0 + P1 + ... for this wave's own 16 fragments, 4 splits per batch
+    // z = P0 + P1 + ... in split order for this wave's own 16 fragments: one
+    // split at a time with all 16 of its fragment loads in flight (one memory
+    // round trip per split, not one per split and fragment). Fragments of
+    // rows past M hold stale bytes (in bounds: whole 128-row blocks) that no
+    // row of the epilogue uses.
+    for (int sp = 0; sp < S; ++sp) {
+      const __amdgpu_buffer_rsrc_t rq = make_rsrc(partial_frag(m, sp, rb, nb, a.row_blocks, 8), 8 * 8 * 1024);
+      u32x4 v[4][4];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+      for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int i2 = 0; i2 < 4; ++i2) {
-        const int f = ((4 * wr + mt) * 8 + 4 * wc + i2) * 64 + lane;
-        if (row_base + 64 * wr + 16 * mt + 4 * g < M) {
-          f32x4 zv = f32x4{0.f, 0.f, 0.f, 0.f};
-          for (int s0 = 0; s0 < S; s0 += 4) {
-            u32x4 v[4];
+        for (int i2 = 0; i2 < 4; ++i2)
+          v[mt][i2] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                    rq, 16 * (((4 * wr + mt) * 8 + 4 * wc + i2) * 64 + lane), 0,
+                                                    kAgentScope));
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-              const __amdgpu_buffer_rsrc_t rq =
-                  make_rsrc(partial_frag(m, min(s0 + u, S - 1), rb, nb, a.row_blocks, 8), 8 * 8 * 1024);
-              v[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, 16 * f, 0, kAgentScope));
-            }
+      for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-            for (int u = 0; u < 4; ++u)
-              if (s0 + u < S)
-                zv = (s0 + u == 0) ? __builtin_bit_cast(f32x4, v[u]) : zv + __builtin_bit_cast(f32x4, v[u]);
-          }
-          z[mt][i2] = zv;
-        }
-      }
+        for (int i2 = 0; i2 < 4; ++i2)
+          z[mt][i2] = sp == 0 ? __builtin_bit_cast(f32x4, v[mt][i2]) : z[mt][i2] + __builtin_bit_cast(f32x4, v[mt][i2]);
+    }
   }
 
   // epilogue: the 128 rows in two passes of 64 through LDS; in each pass
@@ -2077,28 +2077,32 @@ void linear_block_kernel(const LinearArgs a) {
     __syncthreads();
     if (!s_last) return;
     if (threadIdx.x == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    // z = P0 + P1 + ... for this wave's 16 fragments, 4 splits per batch
+    // z = P0 + P1 + ... in split order for this wave's 16 fragments: two
+    // splits at a time with all 32 fragment loads in flight (one memory round
+    // trip per two splits). z starts from +0: +0 + P0 is P0 bit for bit (an
+    // MFMA chain from +0 never ends in -0). Fragments of rows past M hold
+    // stale bytes (in bounds: whole 128-row blocks) that no row of the
+    // epilogue uses.
+    for (int s0 = 0; s0 < S; s0 += 2) {
+      u32x4 v[2][8][TN];
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt)
+      for (int u = 0; u < 2; ++u) {
+        const __amdgpu_buffer_rsrc_t rq = make_rsrc(partial_frag(m, min(s0 + u, S - 1), rb, nb, RB, 8), 8 * 8 * 1024);
 #pragma unroll
-      for (int t = 0; t < TN; ++t) {
-        const int f = (mt * 8 + t0 + t) * 64 + lane;
-        if (row_base + 16 * mt + 4 * g < M) {
-          f32x4 zv = f32x4{0.f, 0.f, 0.f, 0.f};
-          for (int s0 = 0; s0 < S; s0 += 4) {
-            u32x4 v[4];
+        for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-              const __amdgpu_buffer_rsrc_t rq = make_rsrc(partial_frag(m, min(s0 + u, S - 1), rb, nb, RB, 8), 8 * 8 * 1024);
-              v[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, 16 * f, 0, kAgentScope));
-            }
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-              if (s0 + u < S) zv = zv + __builtin_bit_cast(f32x4, v[u]);
-          }
-          z[mt][t] = zv;
-        }
+          for (int t = 0; t < TN; ++t)
+            v[u][mt][t] = __builtin_bit_cast(
+                u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, 16 * ((mt * 8 + t0 + t) * 64 + lane), 0, kAgentScope));
       }
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+        if (s0 + u < S)                                     // uniform
+#pragma unroll
+          for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+            for (int t = 0; t < TN; ++t) z[mt][t] = z[mt][t] + __builtin_bit_cast(f32x4, v[u][mt][t]);
+    }
   }
 
   // epilogue: the block's Z through LDS
