@@ -326,6 +326,7 @@ def main():
 
 
 SECTIONS = ("rows", "mlp128", "prefill", "head")
+MLP_ROWS = (17, 24, 32, 33, 48, 49, 64, 100, 128)      # the 3.5 bpw MLP's mid rows
 
 
 def run_extras(ex, torch, synth, layers, copies, only=None):
@@ -345,27 +346,35 @@ def run_extras(ex, torch, synth, layers, copies, only=None):
 
     if only not in (None, "mlp128"):
         return run_extras_prefill(ex, torch, synth, copies, extra, only)
-    # 27B dense SwiGLU MLP at 3.5 bpw, M = 128: {gate, up} 3-bit group + down 4-bit
-    m = 128
+    # 27B dense SwiGLU MLP at 3.5 bpw: {gate, up} 3-bit group + down 4-bit,
+    # at M = 128 and at the other mid rows of that configuration
     mlp = [synth.gen_layer("bench-mlp", "gate", K, synth.INTERMEDIATE, 3),
            synth.gen_layer("bench-mlp", "up", K, synth.INTERMEDIATE, 3),
            synth.gen_layer("bench-mlp", "down", synth.INTERMEDIATE, K, 4)]
     mc = upload_copies(ex, mlp, 4)
-    xa = x_dev(m, K, 1.0, "mlp-x")
-    xb = x_dev(m, synth.INTERMEDIATE, 1.0, "mlp-x2")
-    wsa = ex.Workspace().reserve(mc[0][:2], m)
-    wsb = ex.Workspace().reserve(mc[0][2:], m)
-    gs = [(Group(ex, c[:2], xa, m, wsa), Group(ex, c[2:], xb, m, wsb)) for c in mc]
-    multi = capture(lambda: [(a.call(), b.call()) for a, b in gs])
-    ms = time_events(multi.replay, 10) / len(gs)
-    fl = flops(mc[0], m)
-    by = alg_bytes(mc[0][:2], m) + alg_bytes(mc[0][2:], m)
-    extra["mlp_M128_TFLOPs"] = round(fl / (ms * 1e-3) / 1e12, 1)
-    extra["mlp_M128_us"] = round(ms * 1e3, 2)
-    extra["mlp_M128_frac_mfma"] = round(fl / (ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)
-    extra["mlp_M128_GBps"] = round(by / (ms * 1e-3) / 1e9, 1)
-    log(f"MLP M=128: {ms * 1e3:.1f} us, {extra['mlp_M128_TFLOPs']} TFLOP/s")
-    del gs, multi, mc
+    wsa = ex.Workspace().reserve(mc[0][:2], 128)
+    wsb = ex.Workspace().reserve(mc[0][2:], 128)
+    rows_us, rows_tf = {}, {}
+    for m in MLP_ROWS:
+        xa = x_dev(m, K, 1.0, "mlp-x")
+        xb = x_dev(m, synth.INTERMEDIATE, 1.0, "mlp-x2")
+        gs = [(Group(ex, c[:2], xa, m, wsa), Group(ex, c[2:], xb, m, wsb)) for c in mc]
+        multi = capture(lambda: [(a.call(), b.call()) for a, b in gs])
+        ms = time_events(multi.replay, 10) / len(gs)
+        fl = flops(mc[0], m)
+        rows_us[m] = round(ms * 1e3, 2)
+        rows_tf[m] = round(fl / (ms * 1e-3) / 1e12, 1)
+        if m == 128:
+            by = alg_bytes(mc[0][:2], m) + alg_bytes(mc[0][2:], m)
+            extra["mlp_M128_TFLOPs"] = rows_tf[m]
+            extra["mlp_M128_us"] = rows_us[m]
+            extra["mlp_M128_frac_mfma"] = round(fl / (ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)
+            extra["mlp_M128_GBps"] = round(by / (ms * 1e-3) / 1e9, 1)
+        log(f"MLP M={m}: {ms * 1e3:.1f} us, {rows_tf[m]} TFLOP/s")
+        del gs, multi
+    extra["mlp_rows_us"] = rows_us
+    extra["mlp_rows_TFLOPs"] = rows_tf
+    del mc
     return run_extras_prefill(ex, torch, synth, copies, extra, only)
 
 

@@ -135,6 +135,13 @@ struct MidChoice {
   bool chained;
 };
 
+// Above 16 rows the spread launch (where its block counts fit) runs one
+// 16-row block after another in one grid, each as at 16 rows, up to this many
+// rows (3-bit {gate, up}: 17-32 rows 57 us against 66 us for the chained
+// 16-row form, 33-48 rows 82-84 against 85-91; at 49-64 rows 108 against 87
+// for the 128-row block tiling).
+constexpr int64_t kSpreadMaxRows = 48;
+
 MidChoice mid_m_choice(int64_t blocks, bool long_chains, int64_t M) {
   const int64_t w16 = blocks * ((M + 15) / 16);            // workgroups of the chained 16-row form
   if (blocks >= 128) return w16 <= 1024 ? MidChoice{1, true} : MidChoice{8, true};
@@ -156,12 +163,33 @@ Launch choose_launch(const MemberPlan *mp, int n, int64_t M) {
     blocks += mp[j].n_blocks;
     long_chains = long_chains || (mp[j].w->K / kChunk) > 16 * mp[j].splits;
   }
+  // one plan S <= 15 for every member: the spread launch is possible
+  int32_t s_uniform = mp[0].splits;
+  for (int j = 1; j < n; ++j)
+    if (mp[j].splits != s_uniform) s_uniform = 0;
+  if (s_uniform > 15) s_uniform = 0;
+  const int64_t ncu = cu_count();
+  // the spread launch's blocks per 16-row block: one own block per CU and
+  // left blocks that the spare waves can take, or 3/4 to 1 block per CU
+  int64_t sp_own = 0, sp_left = 0;
+  if (!all_single && s_uniform > 0 && blocks < kChainedMinBlocks16) {
+    if (blocks > ncu && (blocks - ncu) * s_uniform <= ncu * (16 - s_uniform)) {
+      sp_own = ncu;
+      sp_left = blocks - ncu;
+    } else if (4 * blocks >= 3 * ncu && blocks <= ncu) {
+      sp_own = blocks;
+    }
+  }
   int mt = g_hooks.m_tiles;
   // 16: 128-row tiles two blocks wide; automatic above 128 rows
   const bool wide = mt == 16 || (mt == -1 && M > 128);
   int mid_chained = -1;
+  bool mid_spread = false;
   if (mt == 16) {
     mt = 8;
+  } else if (mt == -1 && M > 16 && M <= kSpreadMaxRows && sp_own > 0) {
+    mt = 1;
+    mid_spread = true;
   } else if (mt == -1 && M > 16 && M <= 128) {
     const MidChoice mc = mid_m_choice(blocks, long_chains, M);
     mt = mc.m_tiles;
@@ -171,38 +199,29 @@ Launch choose_launch(const MemberPlan *mp, int n, int64_t M) {
   }
   L.m_tiles = mt;
   L.row_blocks = (M + 16 * mt - 1) / (16 * mt);
-  // one plan S <= 15 for every member and one 16-row block: the spread
-  // launch is possible
-  int32_t s_uniform = mp[0].splits;
-  for (int j = 1; j < n; ++j)
-    if (mp[j].splits != s_uniform) s_uniform = 0;
-  if (s_uniform > 15) s_uniform = 0;
-  const int64_t ncu = cu_count();
   L.exchange = false;
   bool spread = false;
   if (g_hooks.chained >= 0 && g_hooks.chained <= 3) {
     L.chained = g_hooks.chained == 1 || g_hooks.chained == 2;
-    if (g_hooks.chained == 2 && mt == 1 && L.row_blocks == 1 && s_uniform > 0) {
+    if (g_hooks.chained == 2 && mt == 1 && s_uniform > 0) {
       // forced: as many left blocks as the spare waves can take
       spread = true;
       L.left_blocks = blocks * (16 - s_uniform) / 16;
       L.own_blocks = blocks - L.left_blocks;
     }
+  } else if (mid_spread) {
+    L.chained = spread = true;
+    L.own_blocks = sp_own;
+    L.left_blocks = sp_left;
   } else if (mid_chained >= 0) {
     L.chained = mid_chained == 1 || all_single;
   } else if (mt == 1) {
     if (all_single || blocks >= kChainedMinBlocks16) {
       L.chained = true;
-    } else if (L.row_blocks > 1 || s_uniform == 0) {
-      L.chained = false;
-    } else if (blocks > ncu && (blocks - ncu) * s_uniform <= ncu * (16 - s_uniform)) {
+    } else if (L.row_blocks == 1 && sp_own > 0) {
       L.chained = spread = true;
-      L.own_blocks = ncu;
-      L.left_blocks = blocks - ncu;
-    } else if (4 * blocks >= 3 * ncu && blocks <= ncu) {
-      L.chained = spread = true;
-      L.own_blocks = blocks;
-      L.left_blocks = 0;
+      L.own_blocks = sp_own;
+      L.left_blocks = sp_left;
     } else {
       L.chained = false;
     }
@@ -341,13 +360,13 @@ int exl3_workspace_need(int32_t n_members, const exl3_weight_t *const *w, int64_
   if (e != EXL3_OK) return e;
   size_t rest = 0, cb = 0;
   // sizes grow with M while the launch form stays the same; the row counts
-  // where the automatic choice changes form (16, 32, 48, 96 and 128 rows; the
-  // 16- and 32-row forms also hold the rotation flags) and M itself bound
-  // every smaller call. The counter region sits at a fixed offset, so the
-  // largest counter need and the largest rest add up.
-  const int64_t bounds[6] = {16, 32, 48, 96, 128, M};
-  int64_t probes[6];
-  for (int i = 0; i < 6; ++i) probes[i] = std::min<int64_t>(M, bounds[i]);
+  // where the automatic choice changes form (16, 32, 48, 64, 96 and 128
+  // rows; the 16- and 32-row forms also hold the rotation flags) and M
+  // itself bound every smaller call. The counter region sits at a fixed
+  // offset, so the largest counter need and the largest rest add up.
+  const int64_t bounds[7] = {16, 32, 48, 64, 96, 128, M};
+  int64_t probes[7];
+  for (int i = 0; i < 7; ++i) probes[i] = std::min<int64_t>(M, bounds[i]);
   for (int64_t p : probes)
     if (p > 0) call_need(mp, n_members, p, &rest, &cb);
   *counter_bytes = cb;
@@ -442,7 +461,7 @@ int run_group(int32_t n_members, const exl3_weight_t *const *w, const void *x, i
         : L.kernel == exl3::kQuad128 ? L.row_blocks * ((mp[j].n_blocks + 3) / 4)
                                      : L.row_blocks * mp[j].n_blocks * m.groups;
   }
-  if (L.kernel == exl3::kSpread16) wg = L.own_blocks;
+  if (L.kernel == exl3::kSpread16) wg = L.row_blocks * L.own_blocks;
   if (wg >= (int64_t(1) << 31)) return EXL3_EINVAL;
   la.own_blocks = (int32_t)L.own_blocks;
   la.left_blocks = (int32_t)L.left_blocks;

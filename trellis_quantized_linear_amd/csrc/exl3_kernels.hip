@@ -974,10 +974,15 @@ void linear_spread_kernel(const LinearArgs a) {
   constexpr int P = SB::kLoads <= 2 ? 4 : 2;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int u = blockIdx.x;
+  // workgroup (row block rb, own block u): rows 16 rb .. 16 rb + Mr - 1
+  const int rb = (int)blockIdx.x / a.own_blocks;
+  const int u = (int)blockIdx.x - rb * a.own_blocks;
+  const int RB = a.row_blocks;
   const int S = a.m[0].splits;                           // the same for every member
   const int spare = W - S;                               // waves 0 .. spare-1
   const int M = a.M, K = a.K, C = a.chunks;
+  const int row_base = 16 * rb;
+  const int Mr = min(16, M - row_base);
   const int c = lane & 15, g = lane >> 4;
 
   // LDS: per-wave staging during the chains; afterwards the fold buffers
@@ -1010,7 +1015,7 @@ void linear_spread_kernel(const LinearArgs a) {
   f32x4 acc[1][8];
   if (wave >= spare) {
     const int sp = wave - spare;
-    const ChainCtx<BITS, 1> x = chain_ctx<BITS, 1>(mo, M, K, nbo, 0, lane, true);
+    const ChainCtx<BITS, 1> x = chain_ctx<BITS, 1>(mo, M, K, nbo, row_base, lane, true);
     const int c0 = (int)(((int64_t)sp * C) / S), c1 = (int)(((int64_t)(sp + 1) * C) / S);
     run_chain<BITS, 1, P>(acc, c0, c1, wlds, x, fused,
                           [&] { rot_wait<4>(a, jo, c0 >> 2, (c1 - 1) >> 2, lane, true); });
@@ -1022,20 +1027,20 @@ void linear_spread_kernel(const LinearArgs a) {
       int jl, nbl;
       locate(gb, jl, nbl);
       const MemberArgs &ml = a.m[jl];
-      const ChainCtx<BITS, 1> x = chain_ctx<BITS, 1>(ml, M, K, nbl, 0, lane, true);
+      const ChainCtx<BITS, 1> x = chain_ctx<BITS, 1>(ml, M, K, nbl, row_base, lane, true);
       const int c0 = (int)(((int64_t)sp * C) / S), c1 = (int)(((int64_t)(sp + 1) * C) / S);
       run_chain<BITS, 1, P>(acc, c0, c1, wlds, x, fused,
                             [&] { rot_wait<4>(a, jl, c0 >> 2, (c1 - 1) >> 2, lane, true); });
       // the split's partial, agent scope, then the arrival (see the exchanged launch)
-      const __amdgpu_buffer_rsrc_t rp = make_rsrc(partial_frag(ml, sp, 0, nbl, 1, 1), 8 * 1024);
-      if (4 * g < M) {
+      const __amdgpu_buffer_rsrc_t rp = make_rsrc(partial_frag(ml, sp, rb, nbl, RB, 1), 8 * 1024);
+      if (4 * g < Mr) {
 #pragma unroll
         for (int t = 0; t < 8; ++t)
           __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[0][t]), rp, t * 1024 + 16 * lane, 0,
                                                  kAgentScope);
       }
       __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-      uint32_t *counter = ml.counters + nbl;
+      uint32_t *counter = ml.counters + (int64_t)rb * ml.n_blocks + nbl;
       uint32_t prev = 0;
       if (lane == 0) prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       prev = __builtin_amdgcn_readfirstlane(prev);
@@ -1073,11 +1078,11 @@ void linear_spread_kernel(const LinearArgs a) {
     const MemberArgs &ml = a.m[jl];
     const int fl = f & 63, ft = f >> 6;
     const int fr0 = 4 * (fl >> 4);
-    if (fr0 < M) {
+    if (fr0 < Mr) {
       u32x4 v[15];
 #pragma unroll
       for (int q = 0; q < 15; ++q) {
-        const __amdgpu_buffer_rsrc_t rq = make_rsrc(partial_frag(ml, min(q, S - 1), 0, nbl, 1, 1), 8 * 1024);
+        const __amdgpu_buffer_rsrc_t rq = make_rsrc(partial_frag(ml, min(q, S - 1), rb, nbl, RB, 1), 8 * 1024);
         v[q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, 16 * f, 0, kAgentScope));
       }
       f32x4 zv = __builtin_bit_cast(f32x4, v[0]);
@@ -1102,8 +1107,9 @@ void linear_spread_kernel(const LinearArgs a) {
   __syncthreads();
   // epilogues, 4 rows per wave: waves 0..3 the own block, 4..7 the left block
   if (wave < 4) {
-    if (4 * wave < M)
-      epilogue_rows_lds<1>(zown + 4 * wave * kBlockCols, kBlockCols, eco, lane, mo, nbo * kBlockCols, 4 * wave, M);
+    if (4 * wave < Mr)
+      epilogue_rows_lds<1>(zown + 4 * wave * kBlockCols, kBlockCols, eco, lane, mo, nbo * kBlockCols,
+                           row_base + 4 * wave, M);
   }
   for (int i = 0; i < nleft; ++i) {
     if (i > 0) {
@@ -1114,10 +1120,10 @@ void linear_spread_kernel(const LinearArgs a) {
     int jl, nbl;
     locate(s_left[i], jl, nbl);
     const MemberArgs &ml = a.m[jl];
-    if (wave >= 4 && wave < 8 && 4 * (wave - 4) < M) {
+    if (wave >= 4 && wave < 8 && 4 * (wave - 4) < Mr) {
       const int r4 = 4 * (wave - 4);
       const EpiCols ecl = epi_cols(ml, nbl * kBlockCols, lane);
-      epilogue_rows_lds<1>(zleft + r4 * kBlockCols, kBlockCols, ecl, lane, ml, nbl * kBlockCols, r4, M);
+      epilogue_rows_lds<1>(zleft + r4 * kBlockCols, kBlockCols, ecl, lane, ml, nbl * kBlockCols, row_base + r4, M);
     }
   }
 }
