@@ -424,14 +424,21 @@ def run_extras_head(ex, torch, synth, extra, only):
     m = 16
     head = ex.Weight.from_host(synth.gen_layer("bench-head", "head", K, synth.VOCAB, 6), "cuda")
     xx = x_dev(m, K, 1.0, "head-x")
-    for tag, w in (("head_full", head), ("head_span_A", head.columns(0, 98304))):
-        ws = ex.Workspace().reserve([w], m)
-        g = Group(ex, [w], xx, m, ws)
-        gr = capture(g.call)
-        ms = time_events(gr.replay, 10)
+    # Several calls per graph replay, as the decode step: the full head twice
+    # (963 MB each, past the 256 MB last-level cache); span A (columns
+    # 0..98304, 768 blocks, 381 MB) alternating with the next 768-block span,
+    # which plans alike, so each call streams from HBM.
+    span_a = [head.columns(0, 98304), head.columns(98304, 98304)]
+    for tag, ws_list in (("head_full", [head, head]), ("head_span_A", span_a + span_a)):
+        ws = ex.Workspace().reserve([ws_list[0]], m)
+        gs = [Group(ex, [w], xx, m, ws) for w in ws_list]
+        gr = capture(lambda: [g.call() for g in gs])
+        ms = time_events(gr.replay, 5) / len(gs)
+        w = ws_list[0]
         extra[f"{tag}_M16_GBps"] = round(alg_bytes([w], m) / (ms * 1e-3) / 1e9, 1)
         extra[f"{tag}_M16_us"] = round(ms * 1e3, 2)
         log(f"{tag}: {ms * 1e3:.1f} us, {extra[f'{tag}_M16_GBps']} GB/s")
+        del gs, gr
     # span B is 64 blocks (31.5 MB): cycle 16 distinct 64-block views of the
     # head (504 MB) so it streams from HBM, not from the last-level cache
     views = [head.columns(240128 - 128 * 64 * i, 8192) for i in range(16)]
