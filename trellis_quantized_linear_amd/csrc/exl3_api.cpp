@@ -122,6 +122,13 @@ int cu_count() {
 // several rounds without partials.
 constexpr int64_t kChainedMinBlocks16 = 512;
 
+// Above 16 rows the spread launch (where its block counts fit) runs one
+// 16-row block after another in one grid, each as at 16 rows, up to this many
+// rows (3-bit {gate, up}: 17-32 rows 57 us against 66 us for the chained
+// 16-row form, 33-48 rows 82-84 against 85-91; at 49-64 rows 108 against 87
+// for the 128-row block tiling).
+constexpr int64_t kSpreadMaxRows = 48;
+
 // Mid-M rows (17..128) with the automatic tiling: the row tiling and
 // whether the splits of a block fold inside one workgroup (chained) or
 // exchange through the workspace, chosen from measurements on MI355X of the
@@ -134,13 +141,6 @@ struct MidChoice {
   int m_tiles;
   bool chained;
 };
-
-// Above 16 rows the spread launch (where its block counts fit) runs one
-// 16-row block after another in one grid, each as at 16 rows, up to this many
-// rows (3-bit {gate, up}: 17-32 rows 57 us against 66 us for the chained
-// 16-row form, 33-48 rows 82-84 against 85-91; at 49-64 rows 108 against 87
-// for the 128-row block tiling).
-constexpr int64_t kSpreadMaxRows = 48;
 
 MidChoice mid_m_choice(int64_t blocks, bool long_chains, int64_t M) {
   const int64_t w16 = blocks * ((M + 15) / 16);            // workgroups of the chained 16-row form

@@ -48,7 +48,12 @@ constexpr int kWaitVmcnt0 = 0x0F70;
 constexpr int kAgentScope = 16;
 // Cache policy of the weight stream at up to 32 rows: non-temporal (NT), the
 // words are read once per call and should not displace the rotated input.
+// The spread launch over several 16-row blocks reads each block's words
+// once per row block and keeps the normal policy (3-bit {gate, up}: 32 rows
+// 57 -> 54 us, 48 rows 85 -> 79 us; the normal policy costs 6-8 % at one
+// row block).
 constexpr int kStreamOnce = 2;
+constexpr int kStreamAgain = 0;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, kRsrcWord3);
@@ -759,7 +764,7 @@ struct ChainStage {
   u32x4 b[Stream<BITS, CT>::kLoads];
 };
 
-template <int BITS, int MT, int CT = 8>
+template <int BITS, int MT, int CT = 8, int POL = kStreamOnce>
 __device__ __forceinline__ void load_chain_stage(ChainStage<BITS, MT, CT> &st, __amdgpu_buffer_rsrc_t ra,
                                                  __amdgpu_buffer_rsrc_t rb, const uint32_t (&voff_a)[MT],
                                                  const uint32_t (&voff_b)[Stream<BITS, CT>::kLoads], int chunk,
@@ -771,7 +776,7 @@ __device__ __forceinline__ void load_chain_stage(ChainStage<BITS, MT, CT> &st, _
     st.a[mt] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, (int)voff_a[mt], soff_a, 0));
 #pragma unroll
   for (int l = 0; l < Stream<BITS, CT>::kLoads; ++l)
-    st.b[l] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, (int)voff_b[l], soff_b, kStreamOnce));
+    st.b[l] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, (int)voff_b[l], soff_b, POL));
 }
 
 // Copy a stage's weight bytes into LDS slot `slot` (byte address).
@@ -883,7 +888,7 @@ struct NoWait {
 // region `wlds`; the next chunk is copied to LDS before chunk i is decoded.
 // With `fused` the first P chunks' weight loads go out before ready(), which
 // returns once the chain's part of Xr is written, and their Xr loads after.
-template <int BITS, int MT, int P, int CT = 8, typename Ready = NoWait>
+template <int BITS, int MT, int P, int CT = 8, int POL = kStreamOnce, typename Ready = NoWait>
 __device__ __forceinline__ void run_chain(f32x4 (&acc)[MT][CT], int c0, int c1, char *wlds,
                                           const ChainCtx<BITS, MT, CT> &x, bool fused = false, Ready ready = Ready{}) {
   using SB = Stream<BITS, CT>;
@@ -902,7 +907,7 @@ __device__ __forceinline__ void run_chain(f32x4 (&acc)[MT][CT], int c0, int c1, 
       for (int l = 0; l < SB::kLoads; ++l)
         st[p].b[l] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
                                                    x.rb, (int)x.voff_b[l], min(c0 + p, last) * SB::kFullChunkBytes,
-                                                   kStreamOnce));
+                                                   POL));
     __builtin_amdgcn_sched_barrier(0);
     ready();
     __builtin_amdgcn_sched_barrier(0);
@@ -916,7 +921,7 @@ __device__ __forceinline__ void run_chain(f32x4 (&acc)[MT][CT], int c0, int c1, 
   } else {
 #pragma unroll
     for (int p = 0; p < P; ++p) {
-      load_chain_stage<BITS, MT, CT>(st[p], x.ra, x.rb, x.voff_a, x.voff_b, min(c0 + p, last), x.a_stride);
+      load_chain_stage<BITS, MT, CT, POL>(st[p], x.ra, x.rb, x.voff_a, x.voff_b, min(c0 + p, last), x.a_stride);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -932,7 +937,7 @@ __device__ __forceinline__ void run_chain(f32x4 (&acc)[MT][CT], int c0, int c1, 
       __builtin_amdgcn_sched_barrier(0);
       stage_to_lds<BITS, MT, CT>(st[(p + 1) % P], wlds + ((p + 1) % 2) * SB::kSlot, x.wr_off, x.wrap_off);
       decode_chain_chunk<BITS, MT, CT>(w, st[p], x.shift, x.cb, acc);
-      load_chain_stage<BITS, MT, CT>(st[p], x.ra, x.rb, x.voff_a, x.voff_b, min(c0 + i + p + P, last), x.a_stride);
+      load_chain_stage<BITS, MT, CT, POL>(st[p], x.ra, x.rb, x.voff_a, x.voff_b, min(c0 + i + p + P, last), x.a_stride);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -964,9 +969,8 @@ __device__ __forceinline__ void run_chain(f32x4 (&acc)[MT][CT], int c0, int c1, 
 // gives every CU one block plus one split of the 16 left blocks: 16 busy
 // waves, 4 per SIMD, the same work everywhere.
 
-template <int BITS>
-__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4)))
-void linear_spread_kernel(const LinearArgs a) {
+template <int BITS, int POL>
+__device__ __forceinline__ void spread_body(const LinearArgs &a) {
   using SB = Stream<BITS>;
   constexpr int W = 16, NT = 64 * W;
   // 4 chunks in flight where a chunk is at most two 128-bit loads per lane,
@@ -1017,8 +1021,8 @@ void linear_spread_kernel(const LinearArgs a) {
     const int sp = wave - spare;
     const ChainCtx<BITS, 1> x = chain_ctx<BITS, 1>(mo, M, K, nbo, row_base, lane, true);
     const int c0 = (int)(((int64_t)sp * C) / S), c1 = (int)(((int64_t)(sp + 1) * C) / S);
-    run_chain<BITS, 1, P>(acc, c0, c1, wlds, x, fused,
-                          [&] { rot_wait<4>(a, jo, c0 >> 2, (c1 - 1) >> 2, lane, true); });
+    run_chain<BITS, 1, P, 8, POL>(acc, c0, c1, wlds, x, fused,
+                                  [&] { rot_wait<4>(a, jo, c0 >> 2, (c1 - 1) >> 2, lane, true); });
   } else {
     const int unit = u * spare + wave;
     if (unit < a.left_blocks * S) {
@@ -1029,8 +1033,8 @@ void linear_spread_kernel(const LinearArgs a) {
       const MemberArgs &ml = a.m[jl];
       const ChainCtx<BITS, 1> x = chain_ctx<BITS, 1>(ml, M, K, nbl, row_base, lane, true);
       const int c0 = (int)(((int64_t)sp * C) / S), c1 = (int)(((int64_t)(sp + 1) * C) / S);
-      run_chain<BITS, 1, P>(acc, c0, c1, wlds, x, fused,
-                            [&] { rot_wait<4>(a, jl, c0 >> 2, (c1 - 1) >> 2, lane, true); });
+      run_chain<BITS, 1, P, 8, POL>(acc, c0, c1, wlds, x, fused,
+                                    [&] { rot_wait<4>(a, jl, c0 >> 2, (c1 - 1) >> 2, lane, true); });
       // the split's partial, agent scope, then the arrival (see the exchanged launch)
       const __amdgpu_buffer_rsrc_t rp = make_rsrc(partial_frag(ml, sp, rb, nbl, RB, 1), 8 * 1024);
       if (4 * g < Mr) {
@@ -1126,6 +1130,20 @@ void linear_spread_kernel(const LinearArgs a) {
       epilogue_rows_lds<1>(zleft + r4 * kBlockCols, kBlockCols, ecl, lane, ml, nbl * kBlockCols, row_base + r4, M);
     }
   }
+}
+
+// One 16-row block (streaming word loads), or several (normal policy: the
+// grid reads each block's words once per row block).
+template <int BITS>
+__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4)))
+void linear_spread_kernel(const LinearArgs a) {
+  spread_body<BITS, kStreamOnce>(a);
+}
+
+template <int BITS>
+__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4)))
+void linear_spread_rows_kernel(const LinearArgs a) {
+  spread_body<BITS, kStreamAgain>(a);
 }
 
 // ------------------------------------------------------------ linear, 16 and 32 rows per workgroup
@@ -2371,8 +2389,8 @@ constexpr LinearFn pick_kernel(int kernel) {
 }
 
 template <int BITS>
-LinearFn pick_linear(int kernel, bool chained) {
-  if (kernel == kSpread16) return linear_spread_kernel<BITS>;
+LinearFn pick_linear(int kernel, bool chained, int rows) {
+  if (kernel == kSpread16) return rows > 1 ? linear_spread_rows_kernel<BITS> : linear_spread_kernel<BITS>;
   if (kernel == kChain16x8) return linear_chain_kernel<BITS, 1, true, 8>;
   if (kernel == kChain16H) return linear_chain_kernel<BITS, 1, false, 8, 4>;
   if (kernel == kWide128) return linear_wide_kernel<BITS>;
@@ -2390,13 +2408,13 @@ int launch_linear(const LinearArgs &a, int bits, int kernel, bool chained, void 
     return (int)hipErrorInvalidValue;
   LinearFn fn = nullptr;
   switch (bits) {
-    case 2: fn = pick_linear<2>(kernel, chained); break;
-    case 3: fn = pick_linear<3>(kernel, chained); break;
-    case 4: fn = pick_linear<4>(kernel, chained); break;
-    case 5: fn = pick_linear<5>(kernel, chained); break;
-    case 6: fn = pick_linear<6>(kernel, chained); break;
-    case 7: fn = pick_linear<7>(kernel, chained); break;
-    case 8: fn = pick_linear<8>(kernel, chained); break;
+    case 2: fn = pick_linear<2>(kernel, chained, a.row_blocks); break;
+    case 3: fn = pick_linear<3>(kernel, chained, a.row_blocks); break;
+    case 4: fn = pick_linear<4>(kernel, chained, a.row_blocks); break;
+    case 5: fn = pick_linear<5>(kernel, chained, a.row_blocks); break;
+    case 6: fn = pick_linear<6>(kernel, chained, a.row_blocks); break;
+    case 7: fn = pick_linear<7>(kernel, chained, a.row_blocks); break;
+    case 8: fn = pick_linear<8>(kernel, chained, a.row_blocks); break;
     default: return (int)hipErrorInvalidValue;
   }
   (void)hipGetLastError();   // report this launch's error, not an earlier one
