@@ -46,12 +46,14 @@ constexpr int kWaitVmcnt0 = 0x0F70;
 // workgroups: SC1, agent scope (written through / fetched past the XCD's
 // non-coherent L2), the same bit LLVM sets for agent-scope atomics here.
 constexpr int kAgentScope = 16;
-// Cache policy of the weight stream at up to 32 rows: non-temporal (NT), the
-// words are read once per call and should not displace the rotated input.
-// The spread launch over several 16-row blocks reads each block's words
-// once per row block and keeps the normal policy (3-bit {gate, up}: 32 rows
-// 57 -> 54 us, 48 rows 85 -> 79 us; the normal policy costs 6-8 % at one
-// row block).
+// Cache policy of the weight stream of the 16- and 32-row launches of one
+// row block: non-temporal (NT), the words are read once per call and should
+// not displace the rotated input. A launch over several row blocks reads
+// each block's words once per row block and keeps the normal policy, so the
+// later row blocks find them in the last-level cache (3-bit {gate, up}
+// spread launch at 32 / 48 rows 57 -> 54 / 85 -> 79 us; chained or
+// exchanged 16-row forms: q/k/v at 24 rows 18.4 -> 16.6 us, down at 40 rows
+// 34.2 -> 30.2 us; the normal policy costs 6-8 % at one row block).
 constexpr int kStreamOnce = 2;
 constexpr int kStreamAgain = 0;
 
@@ -1152,7 +1154,7 @@ void linear_spread_rows_kernel(const LinearArgs a) {
 // CT = 4 (exchanged, 16 rows, W = 8): the two waves 2i, 2i+1 share split i of
 // the workgroup, each with 4 of the block's 8 column tiles: the same MFMA
 // chains, two waves per SIMD where one wave per split would leave one.
-template <int BITS, int MT, bool CHAINED, int W, int CT = 8>
+template <int BITS, int MT, bool CHAINED, int W, int CT = 8, int POL = kStreamOnce>
 __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(W == 8 ? 4 : 1)))
 void linear_chain_kernel(const LinearArgs a) {
   static_assert(CT == 8 || (CT == 4 && !CHAINED && MT == 1), "column halves: exchanged 16-row tiles only");
@@ -1213,7 +1215,7 @@ void linear_chain_kernel(const LinearArgs a) {
       // in 128 VGPRs (W = 8) only 2 chunks of more than two 128-bit loads fit
       constexpr int P = (W == 8 && SB::kLoads > 2) ? 2 : ChainDepth<MT>::P;
       const int c0 = (int)(((int64_t)s * C) / S), c1 = (int)(((int64_t)(s + 1) * C) / S);
-      run_chain<BITS, MT, P, CT>(acc, c0, c1, wlds, x, fused,
+      run_chain<BITS, MT, P, CT, POL>(acc, c0, c1, wlds, x, fused,
                              [&] { rot_wait<4 * MT>(a, j, c0 >> 2, (c1 - 1) >> 2, lane, false); });
     }
     if constexpr (CHAINED) {
@@ -2380,10 +2382,14 @@ __global__ void fill_zero_kernel(uint32_t *p, int64_t n) {
 
 typedef void (*LinearFn)(const LinearArgs);
 
+// rows: row blocks of the launch (several: the normal policy on the 16- and
+// 32-row forms' word loads)
 template <int BITS, bool CHAINED>
-constexpr LinearFn pick_kernel(int kernel) {
-  return kernel == kChain16   ? linear_chain_kernel<BITS, 1, CHAINED, 4>
-       : kernel == kChain32   ? linear_chain_kernel<BITS, 2, CHAINED, 4>
+constexpr LinearFn pick_kernel(int kernel, int rows) {
+  return kernel == kChain16   ? (rows > 1 ? linear_chain_kernel<BITS, 1, CHAINED, 4, 8, kStreamAgain>
+                                          : linear_chain_kernel<BITS, 1, CHAINED, 4>)
+       : kernel == kChain32   ? (rows > 1 ? linear_chain_kernel<BITS, 2, CHAINED, 4, 8, kStreamAgain>
+                                          : linear_chain_kernel<BITS, 2, CHAINED, 4>)
        : kernel == kNtile64   ? linear_ntile_kernel<BITS, 4, CHAINED>
                               : linear_tile_kernel<BITS, CHAINED>;
 }
@@ -2391,12 +2397,14 @@ constexpr LinearFn pick_kernel(int kernel) {
 template <int BITS>
 LinearFn pick_linear(int kernel, bool chained, int rows) {
   if (kernel == kSpread16) return rows > 1 ? linear_spread_rows_kernel<BITS> : linear_spread_kernel<BITS>;
-  if (kernel == kChain16x8) return linear_chain_kernel<BITS, 1, true, 8>;
-  if (kernel == kChain16H) return linear_chain_kernel<BITS, 1, false, 8, 4>;
+  if (kernel == kChain16x8)
+    return rows > 1 ? linear_chain_kernel<BITS, 1, true, 8, 8, kStreamAgain> : linear_chain_kernel<BITS, 1, true, 8>;
+  if (kernel == kChain16H)
+    return rows > 1 ? linear_chain_kernel<BITS, 1, false, 8, 4, kStreamAgain> : linear_chain_kernel<BITS, 1, false, 8, 4>;
   if (kernel == kWide128) return linear_wide_kernel<BITS>;
   if (kernel == kBlock128) return chained ? linear_block_kernel<BITS, true> : linear_block_kernel<BITS, false>;
   if (kernel == kQuad128) return linear_quad_kernel<BITS>;
-  return chained ? pick_kernel<BITS, true>(kernel) : pick_kernel<BITS, false>(kernel);
+  return chained ? pick_kernel<BITS, true>(kernel, rows) : pick_kernel<BITS, false>(kernel, rows);
 }
 
 }  // namespace
