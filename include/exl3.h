@@ -122,7 +122,9 @@ int exl3_weight_columns(const exl3_weight_t *parent, int64_t col_from, int64_t n
  * one call of exl3_linear_group with these members at M rows needs. The
  * counter region holds the split counters and, for calls of up to 32 rows,
  * the rotated-input chunk flags; all are zero between calls. Sizing a
- * workspace for the largest M it will see covers every smaller M.
+ * workspace for the largest M it will see covers every smaller M under the
+ * automatic launch choice (a launch forced through exl3_test_force may need
+ * more: size under the same hooks).
  * Errors: as exl3_linear_group's argument checks. */
 int exl3_workspace_need(int32_t n_members, const exl3_weight_t *const *w, int64_t M,
                         size_t *bytes, size_t *counter_bytes);
@@ -234,9 +236,11 @@ int exl3_test_fuse_rotation(int32_t on, int32_t spin_limit);
  *            choice above 128 rows; chained launches only, else as 8);
  *   chained: -1 automatic, 0 one K split per workgroup with counter exchange,
  *            1 every split of a block in one workgroup, summed in order,
- *            2 the spread launch (up to 16 rows, one S <= 15 for every
- *            member; otherwise as 1): a 16-wave workgroup per owned block,
- *            its spare waves taking splits of the remaining blocks,
+ *            2 the spread launch (16-row tiles, one S <= 15 for every
+ *            member; otherwise as 1): a 16-wave workgroup per (16-row block,
+ *            owned block), its spare waves taking splits of the remaining
+ *            blocks (the automatic choice at up to 48 rows where the block
+ *            counts fit, e.g. the {gate, up} pair),
  *            3 as 0, with each split on two waves of 4 column tiles (16-row
  *            tiles; the automatic choice when 16-row exchanged launches have
  *            at most one split chain per SIMD).
