@@ -971,7 +971,10 @@ __device__ __forceinline__ void run_chain(f32x4 (&acc)[MT][CT], int c0, int c1, 
 // gives every CU one block plus one split of the 16 left blocks: 16 busy
 // waves, 4 per SIMD, the same work everywhere.
 
-template <int BITS, int POL>
+// ROWS: several 16-row blocks (row block and its bounds at run time; one
+// row block keeps them compile-time constants, which the left blocks'
+// partial addressing folds away)
+template <int BITS, int POL, bool ROWS>
 __device__ __forceinline__ void spread_body(const LinearArgs &a) {
   using SB = Stream<BITS>;
   constexpr int W = 16, NT = 64 * W;
@@ -981,14 +984,14 @@ __device__ __forceinline__ void spread_body(const LinearArgs &a) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   // workgroup (row block rb, own block u): rows 16 rb .. 16 rb + Mr - 1
-  const int rb = (int)blockIdx.x / a.own_blocks;
+  const int rb = ROWS ? (int)blockIdx.x / a.own_blocks : 0;
   const int u = (int)blockIdx.x - rb * a.own_blocks;
-  const int RB = a.row_blocks;
+  const int RB = ROWS ? a.row_blocks : 1;
   const int S = a.m[0].splits;                           // the same for every member
   const int spare = W - S;                               // waves 0 .. spare-1
   const int M = a.M, K = a.K, C = a.chunks;
   const int row_base = 16 * rb;
-  const int Mr = min(16, M - row_base);
+  const int Mr = ROWS ? min(16, M - row_base) : M;
   const int c = lane & 15, g = lane >> 4;
 
   // LDS: per-wave staging during the chains; afterwards the fold buffers
@@ -1139,13 +1142,13 @@ __device__ __forceinline__ void spread_body(const LinearArgs &a) {
 template <int BITS>
 __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4)))
 void linear_spread_kernel(const LinearArgs a) {
-  spread_body<BITS, kStreamOnce>(a);
+  spread_body<BITS, kStreamOnce, false>(a);
 }
 
 template <int BITS>
 __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4)))
 void linear_spread_rows_kernel(const LinearArgs a) {
-  spread_body<BITS, kStreamAgain>(a);
+  spread_body<BITS, kStreamAgain, true>(a);
 }
 
 // ------------------------------------------------------------ linear, 16 and 32 rows per workgroup
