@@ -21,6 +21,8 @@
  *     detected on the host before anything is launched, except EXL3_EHIP,
  *     which reports a failed HIP launch (exl3_last_hip_error() gives the HIP
  *     code). No C++ exception crosses this boundary.
+ *   - Size: M * K * 2 < 2^31 per call (the rotated input of one member, fp16,
+ *     stays under 2 GiB: the kernels address it with 32-bit offsets).
  *   - Arithmetic is fixed: the rotated input is fp16, weights are fp16, K
  *     sums are fp32 in one canonical order, outputs are bf16. Row m of Y is
  *     byte-identical for every row count M, every row regime, group
@@ -55,7 +57,8 @@ extern "C" {
 
 /* Error codes. */
 #define EXL3_OK          0
-#define EXL3_EINVAL     (-1)  /* null pointer, negative M, ldx < K, ldy < N, n_cols < 0 */
+#define EXL3_EINVAL     (-1)  /* null pointer, negative M, ldx < K, ldy < N, n_cols < 0,
+                                 M * K * 2 >= 2^31 (one member's rotated input past 2 GiB) */
 #define EXL3_EALIGN     (-2)  /* K or N not a multiple of 128, view not whole blocks,
                                  misaligned pointer (words and workspace: 4 bytes;
                                  fp16/bf16 arrays: 2 bytes), block_stride too small */

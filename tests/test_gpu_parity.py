@@ -335,3 +335,35 @@ def test_width_and_shape_sweep_mid_rows(bits):
         for r in (0, M - 1):
             one = G.host_u16(G.run(w, xd[r:r + 1], M=1, tag=f"sweep row {r}"))
             assert np.array_equal(one[0], full[r]), (K, N, bits, M, r)
+
+
+def test_prompt_rows_at_the_size_limit():
+    """Largest call: M K 2 < 2^31 bytes of rotated input per member (the
+    library's 32-bit offsets), so at K = 5120 at most 209,715 rows; the
+    128-row tilings read that input chunk-major up to the last chunk offset.
+    X repeats 1024 seeded rows: sampled rows against the oracle, rows a
+    multiple of 1024 apart byte-identical. One row more is refused
+    (EXL3_EINVAL) before anything is launched."""
+    torch = G.torch_mod()
+    K, N, M = 5120, 128, 209715
+    L = G.layer("size-limit", "w", K, N, 4)
+    w = G.upload(L)
+    base = G.xbits("size-limit", 1024, K)
+    xd = G.dev_bf16(base).repeat((M + 1 + 1023) // 1024, 1)[:M + 1].contiguous()
+    y = G.empty_y(M + 1, N)
+    ws = ex().Workspace().reserve([w], M)
+    G.say(f"exl3_linear K={K} N={N} M={M} (2KM = {2 * K * M}, limit {2 ** 31})")
+    ex().exl3_linear(w, xd, y, ws, M=M)
+    torch.cuda.synchronize()
+    yh = G.host_u16(y)
+    rows = [0, 1, 1023, 1024 * 100 + 7, M - 1]
+    ref = G.oracle_blocks(L, base, [0], rows=[r % 1024 for r in rows])
+    G.assert_close(yh[rows], ref, what=f"M={M}")
+    for r in (5, 1000, M - 1):
+        assert np.array_equal(yh[r], yh[r % 1024]), r
+    last = yh[M].copy()
+    with pytest.raises(ex().Exl3Error) as e:
+        ex().exl3_linear(w, xd, y, ws, M=M + 1)
+    assert e.value.code == ex().EXL3_EINVAL
+    torch.cuda.synchronize()
+    assert np.array_equal(G.host_u16(y)[M], last)

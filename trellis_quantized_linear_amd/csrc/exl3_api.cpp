@@ -477,7 +477,8 @@ int run_group(int32_t n_members, const exl3_weight_t *const *w, const void *x, i
   // contiguous 8 KB (the 3-bit {gate, up} pair at 128 rows: 121 -> 100 us).
   // The spread launch reads chunk-major too (its 16 rows as 8 whole lines);
   // the other 16- to 64-row launches measured as fast or faster row-major.
-  // Chunk offsets are 32-bit: chunk-major needs 2 K M < 2^31.
+  // Chunk offsets are 32-bit: chunk-major needs 2 K M < 2^31, which every
+  // accepted call meets (check_group).
   const bool tile_cm = (L.kernel == exl3::kTile128 || L.kernel == exl3::kBlock128 || L.kernel == exl3::kWide128 ||
                         L.kernel == exl3::kQuad128) &&
                        2 * K * M < (int64_t(1) << 31);
