@@ -313,6 +313,19 @@ def test_rotation_runs_inside_the_linear_launch_up_to_32_rows(lib):
         for M in (17, 32):
             assert launches(M) == 1, M
         ex.exl3_test_force(-1, -1, 0)
+        # the {gate, up} pair: one launch at 16 rows (spread launch, one row
+        # block); at 17-48 rows the spread launch covers several row blocks
+        # and keeps its rotation launch
+        g = fake_weight(5120, 17408, 4, base=0x60000000)
+        u = fake_weight(5120, 17408, 4, base=0x70000000)
+        gu = ex._wlist([g, u])
+        need2, cb2 = ex.exl3_workspace_need([g, u], 48)
+        ws2 = ex.exl3_workspace_t(0x20000000, need2, cb2)
+        ys2 = (ctypes.c_void_p * 2)(0x80000000, 0x90000000)
+        ld2 = (ctypes.c_int64 * 2)(17408, 17408)
+        for M, n in ((16, 1), (17, 2), (48, 2)):
+            assert lib.exl3_linear_group(2, gu, 0x30000000, 5120, M, ys2, ld2, ctypes.byref(ws2), None) == 0
+            assert ex.exl3_test_mock_counts()[0] == n, M
         # the two-phase calls never fuse
         assert lib.exl3_rotate(3, arr, 0x30000000, 5120, 16, ctypes.byref(ws), None) == 0
         assert lib.exl3_linear_rotated(3, arr, 16, ys, ld, ctypes.byref(ws), None) == 0
