@@ -378,6 +378,26 @@ def check_special_values_propagate():
     assert np.all(~np.isfinite(y2[0, 128:])) and np.all(np.isfinite(y2[0, :128]))
 
 
+def check_rows_independent():
+    """Row independence, the pages' "window outputs equal step outputs"
+    (TensorFold PR #1467, "Receipt": window logits equal step logits byte for
+    byte): the oracle at M = 7 rows gives, row for row, the bytes of seven
+    one-row calls, and the rows of a column view those of the full weight's
+    columns (K = 256, N = 384, 3 bits)."""
+    from trellis_quantized_linear_amd import synth
+    K, N, bits = 256, 384, 3
+    L = synth.gen_layer("rows-independent", "w", K, N, bits)
+    x = synth.gen_x(synth.rng_for("rows-independent", "x", 7), 7, K)
+    full = O.linear_packed(L.words, K, N, bits, L.scales, L.suh, L.svh, x)
+    for r in range(7):
+        one = O.linear_packed(L.words, K, N, bits, L.scales, L.suh, L.svh, x[r:r + 1])
+        assert np.array_equal(one[0], full[r]), r
+    bs = O.block_bytes(K, bits)
+    view = O.linear_packed(L.words, K, 128, bits, L.scales[256:384], L.suh, L.svh[256:384], x,
+                           block_stride=bs, offset=2 * bs)
+    assert np.array_equal(view, full[:, 256:384])
+
+
 ALL_CHECKS = [
     check_fp16_decode_all_patterns, check_fp16_round_vs_numpy,
     check_bf16_decode_all_patterns, check_bf16_round_vs_torch,
@@ -386,5 +406,5 @@ ALL_CHECKS = [
     check_tile_placement, check_view_decode_equals_parent_columns, check_head_byte_accounting,
     check_fwht_closed_form, check_rot_in_one_hot,
     check_dense_brute_force, check_constant_weight_closed_form, check_fp32_stress_exceeds_fp16,
-    check_special_values_propagate,
+    check_special_values_propagate, check_rows_independent,
 ]
