@@ -251,6 +251,32 @@ def test_workspace_for_max_rows_covers_smaller_calls(lib):
     ex.exl3_test_mock_counts()
 
 
+def test_group_workspace_for_max_rows_covers_smaller_calls(lib):
+    """The same for groups, at every row count where the automatic choice
+    changes form (the {gate, up} pair takes the spread launch up to 48 rows,
+    over several 16-row blocks above 16, then the 128-row block tiling; the
+    {q, k, v} group the 16-row forms, then 128-row tiles)."""
+    ex.exl3_test_mock(True)
+    groups = [[fake_weight(5120, 17408, b), fake_weight(5120, 17408, b, base=0x50000000)] for b in (3, 4)]
+    groups.append([fake_weight(5120, 6144, 4), fake_weight(5120, 1024, 4, base=0x50000000),
+                   fake_weight(5120, 1024, 4, base=0x60000000)])
+    rows = (1, 7, 16, 17, 24, 32, 33, 40, 47, 48, 49, 64, 65, 96, 97, 100, 128, 129, 256)
+    for ws_ in groups:
+        n = len(ws_)
+        arr = ex._wlist(ws_)
+        ys = (ctypes.c_void_p * n)(*[0x80000000 + 0x10000000 * j for j in range(n)])
+        ld = (ctypes.c_int64 * n)(*[w.N for w in ws_])
+        for max_rows in (16, 32, 40, 48, 64, 100, 128, 300):
+            need, cb = ex.exl3_workspace_need(ws_, max_rows)
+            ws = ex.exl3_workspace_t(0x20000000, need, cb)
+            for M in sorted(set(rows) | {max_rows}):
+                if M > max_rows:
+                    continue
+                rc = lib.exl3_linear_group(n, arr, 0x30000000, 5120, M, ys, ld, ctypes.byref(ws), None)
+                assert rc == 0, ([w.N for w in ws_], max_rows, M, rc)
+    ex.exl3_test_mock_counts()
+
+
 def test_workspace_grow_errors(lib):
     ws = ex.exl3_workspace_t(0, 0, 0)
     assert lib.exl3_workspace_grow(ctypes.byref(ws), 0x20000001, 1024, 256, None) == ex.EXL3_EALIGN
