@@ -112,8 +112,9 @@ typedef struct exl3_workspace {
 int exl3_plan(int64_t K, int64_t N, int32_t bits, exl3_plan_t *out);
 
 /* exl3_weight_columns — a view of columns [col_from, col_from + n_cols) of
- * `parent`, made of whole 128-column blocks, that keeps the parent's strides
- * and moves its pointers to its first block (PR #1507, "What this changes").
+ * `parent`, made of whole 128-column blocks: its descriptor carries the
+ * parent's block stride and points at the view's first block (PR #1507,
+ * "What this changes").
  * It copies nothing and lives no longer than the parent's buffers.
  * Errors: EINVAL (NULL pointers, n_cols <= 0), EALIGN (col_from or n_cols
  * not a multiple of 128), ERANGE (outside the parent), and the parent's own
@@ -148,10 +149,13 @@ int exl3_workspace_grow(exl3_workspace_t *ws, void *ptr, size_t bytes, size_t co
 int exl3_workspace_reset(const exl3_workspace_t *ws, void *stream);
 
 /* exl3_linear — Y[M x N] = rot_out(dequant(W) . rot_in(X)) for one weight or
- * view. M == 0 returns EXL3_OK and launches nothing. Two launches on
- * `stream`: the input rotation, then the linear (decode + MFMA + split-K
- * exchange + epilogue); see exl3_test_fuse_rotation for the one-launch form
- * at up to 32 rows. Never allocates, memsets or synchronises, so it may be
+ * view: the per-weight EXL3 linear of any row count (PR #1467, "What this
+ * changes" and "The arithmetic": decode rows and 17-128-row forms with one
+ * set of bits), its split-K partials met through counters that the last
+ * arriving workgroup resets (PR #1475, "What this changes"). M == 0 returns
+ * EXL3_OK and launches nothing. Two launches on `stream`: the input rotation,
+ * then the linear (decode + MFMA + split-K exchange + epilogue); see
+ * exl3_test_fuse_rotation for the one-launch form at up to 32 rows. Never allocates, memsets or synchronises, so it may be
  * captured in a HIP graph. Calls that run concurrently (other streams) must
  * use different workspaces.
  * Errors: EINVAL, EALIGN, EBITS, EWORKSPACE, EHIP. */

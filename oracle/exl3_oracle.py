@@ -30,14 +30,15 @@ print neither the codebook nor the bit layout.  What they do fix, and where:
   * decoded weights are fp16 and K sums are fp32; a constant weight times
     rotated inputs of 4096 overflows fp16 sums but not fp32 ones
     (PR #1467, author follow-up on the kernel contract, gate 4);
-  * at odd widths the code windows begin at odd bit offsets, so a 0xaaaa
-    fill decodes to two alternating weights at 3 and 5 bits, while all-ones
-    states with unit scales decode to one weight at every width (PR #1467,
+  * the stress fill of the kernel contract: with unit scales, a stream of
+    all set bits yields a single weight value whatever the width, whereas the
+    alternating pattern 0xaaaa yields two values in turn at widths 3 and 5,
+    since odd widths start their windows on odd bit positions (PR #1467,
     author follow-up, gate 4, after the width-matrix review);
   * per-column scales and a per-member input sign vector suh (PR #1467, gates
     and planted controls that swap one group member's scales or its suh);
-  * column views are whole 128-column blocks that keep the parent's strides
-    (PR #1507, "What this changes");
+  * a column view spans whole 128-column blocks and addresses them with the
+    strides of the weight it is cut from (PR #1507, "What this changes");
   * planted NaN and both infinities reach the outputs (PR #1467, gate 1).
 
 Everything else (16-bit state width, LSB-first bit order, the column-major
@@ -189,8 +190,8 @@ def decode(words, K: int, N: int, bits: int, block_stride: int | None = None,
     Inside a tile, weight i sits at K row i mod 16 and column floor(i/16): the
     stream walks down a column first.  A column view of whole blocks is the
     same call with `offset` moved by whole blocks and the parent's
-    `block_stride` (column views keep the parent's strides: PR #1507, "What this
-    changes").
+    `block_stride` (a view addresses its blocks with the full weight's strides:
+    PR #1507, "What this changes").
     """
     assert K % 128 == 0 and N % BLOCK_COLS == 0 and 1 <= bits <= 8
     if block_stride is None:
@@ -275,23 +276,3 @@ def linear_packed(words, K, N, bits, scales_fp16, suh_fp16, svh_fp16, x_bf16,
     """Decode then apply: the whole path for one weight or column view."""
     W = decode(words, K, N, bits, block_stride=block_stride, offset=offset)
     return linear(W, scales_fp16, suh_fp16, svh_fp16, x_bf16, exact=exact)
-
-
-def linear_group(members, x_bf16) -> list:
-    """Group of members sharing X: each member's own result (the group launch
-    is defined as each member's own launch; PR #1467, "The arithmetic").
-    `members` is a list of dicts with keys words, K, N, bits, scales, suh, svh
-    and optionally block_stride, offset."""
-    out = []
-    for m in members:
-        out.append(linear_packed(m["words"], m["K"], m["N"], m["bits"], m["scales"],
-                                 m["suh"], m["svh"], x_bf16,
-                                 block_stride=m.get("block_stride"),
-                                 offset=m.get("offset", 0)))
-    return out
-
-
-def algorithmic_bytes(K: int, N: int, bits: int, M: int, with_x: bool = True) -> int:
-    """Bytes the method must move for one weight at M rows: packed words,
-    fp16 scales, suh and svh, bf16 X (once per group) and bf16 Y."""
-    return packed_bytes(K, N, bits) + 2 * N + 2 * K + 2 * N + (2 * M * K if with_x else 0) + 2 * M * N

@@ -159,10 +159,10 @@ def check_windows_random_vs_strings():
 
 
 def check_fills_from_the_pages():
-    """TensorFold PR #1467 (gate 4): all-ones states decode to one weight at
-    every width; a 0xaaaa fill decodes to two alternating weights at 3 and 5
-    bits because their windows start at odd offsets (and to one weight at even
-    widths)."""
+    """TensorFold PR #1467 (gate 4 stress fills): a stream of set bits gives a
+    single weight value at any width; the 0xaaaa pattern gives two values in
+    turn at widths 3 and 5, whose windows start on odd bit positions, and a
+    single value at the even widths."""
     for bits in range(2, 9):
         n = 32 * bits
         ones = O.codebook(O.tile_states(np.full(n, 0xFF, np.uint8), bits))

@@ -264,7 +264,7 @@ def test_two_streams_equal_solo():
 
 def test_split_exchange_stress():
     """Race check of the counter protocol: 2000 back-to-back calls of a narrow
-    weight (32 splits per block, exchange through partials) on one stream,
+    weight (the plan's 16 splits per block, exchange through partials) on one stream,
     bytes compared every 100 calls and counters zero at the end."""
     torch = G.torch_mod()
     K, N = 5120, 1024

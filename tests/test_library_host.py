@@ -104,8 +104,9 @@ def test_plan_errors(lib):
 
 
 def test_view_keeps_parent_strides_and_moves_to_first_block(lib):
-    """PR #1507 host test: a column view keeps the parent's strides and moves
-    to its first 128-column block."""
+    """PR #1507 host test: a view's descriptor carries the full weight's
+    block stride, and its pointers start at the view's first 128-column
+    block."""
     w = fake_weight(5120, 248320, 6)
     v = w.columns(240128, 8192)
     bs = 16 * 5120 * 6

@@ -17,8 +17,9 @@
 // every group and every column view runs the same per-output arithmetic: one
 // MFMA shape, the same K chunks per split in ascending order, the splits added
 // left to right in fp32, and one epilogue routine. A row's bits therefore do
-// not depend on the row count (PR #1467, "The arithmetic": the mid-M kernels,
-// the group launch and rot_group return the bytes of the one-weight launch).
+// not depend on the row count (PR #1467, "The arithmetic": every mid-M form,
+// a group member and the group rotation produce exactly what the single-weight
+// launch produces).
 #include <hip/hip_runtime.h>
 
 #include <type_traits>

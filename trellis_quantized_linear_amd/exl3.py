@@ -121,6 +121,16 @@ def _stream_handle(stream) -> Optional[int]:
     return stream.cuda_stream or None
 
 
+def _torch_stream(stream):
+    """The torch stream object for a stream argument (None: the current one)."""
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream()
+    if isinstance(stream, int):
+        return torch.cuda.ExternalStream(stream)
+    return stream
+
+
 def _ptr(t) -> int:
     return 0 if t is None else int(t.data_ptr())
 
@@ -187,13 +197,26 @@ class Workspace:
     `reserve` sizes it for some members up to `max_rows` rows; growth
     allocates a new buffer and lets the library zero its counters once on the
     given stream. Linear calls themselves never allocate.
+
+    A replaced buffer is handed back to torch's allocator marked as in use by
+    the growth's stream (record_stream), so its memory is reused only after
+    the work queued there before the growth has finished. Calls on other
+    streams must be ordered before the growth by the caller. With
+    keep_retired=True replaced buffers are kept instead (for HIP graphs
+    captured before a growth, which hold the old address) until
+    release_retired().
     """
 
-    def __init__(self, device="cuda"):
+    def __init__(self, device="cuda", keep_retired: bool = False):
         self.device = device
         self.ws = exl3_workspace_t(None, 0, 0)
         self.buf = None
-        self.retired = []        # old buffers kept until the caller syncs
+        self.keep_retired = keep_retired
+        self.retired = []
+
+    def release_retired(self):
+        """Drop buffers kept by keep_retired=True (once nothing uses them)."""
+        self.retired = []
 
     def reserve(self, weights: Sequence[Weight], max_rows: int, stream=None):
         import torch
@@ -209,7 +232,10 @@ class Workspace:
         _check(lib().exl3_workspace_grow(ctypes.byref(self.ws), _ptr(buf), total, cb, _stream_handle(stream)),
                "exl3_workspace_grow")
         if self.buf is not None:
-            self.retired.append(self.buf)
+            if self.keep_retired:
+                self.retired.append(self.buf)
+            else:
+                self.buf.record_stream(_torch_stream(stream))
         self.buf = buf
         return self
 
