@@ -21,12 +21,17 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950", "-ffp-contract=
           "-fno-gpu-flush-denormals-to-zero", "-I", INCLUDE, "-I", CSRC]
 DEVICE = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
-SOURCES = ["exl3_kernels.hip", "exl3_api.cpp"]
+# (source, extra flags): the linear kernels compile once per bit width, in
+# parallel with the rest
+SOURCES = [("exl3_kernels.hip", []), ("exl3_api.cpp", [])] + \
+          [("exl3_linear_bits.hip", [f"-DEXL3_BITS={b}", f"-cuid=exl3_linear_bits_{b}"]) for b in range(2, 9)]
 
 
-def _compile(src: str, build_dir: str) -> str:
-    obj = os.path.join(build_dir, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *COMMON, *(DEVICE if src.endswith(".hip") else []), "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(job, build_dir: str) -> str:
+    src, extra = job
+    tag = "".join(ch for ch in extra[0] if ch.isalnum()).lower() if extra else ""
+    obj = os.path.join(build_dir, os.path.basename(src) + (("." + tag) if tag else "") + ".o")
+    cmd = [HIPCC, *COMMON, *(DEVICE if src.endswith(".hip") else []), *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
@@ -37,7 +42,8 @@ def _compile(src: str, build_dir: str) -> str:
 def build(verbose: bool = False) -> str:
     build_dir = os.path.join(ROOT, "_build")
     os.makedirs(build_dir, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+    workers = max(1, min(len(SOURCES), len(os.sched_getaffinity(0)), 16))
+    with ThreadPoolExecutor(max_workers=workers) as ex:
         objs = list(ex.map(lambda s: _compile(s, build_dir), SOURCES))
     tmp = LIB + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]

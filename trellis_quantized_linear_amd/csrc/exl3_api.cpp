@@ -272,7 +272,12 @@ Layout layout_for(const MemberPlan *mp, int n, int64_t M, int64_t K, const Launc
   Layout lay{};
   for (int j = 0; j < n; ++j) {
     lay.xr_bytes[j] = align_up((size_t)M * K * 2);
-    if (L.exchange) {
+    if (L.exchange && L.kernel == exl3::kSpread16) {
+      // the spread launch: partials of the left blocks only, all members'
+      // in member 0's buffer ([split][row block][left block][16 x 128])
+      if (j == 0) lay.part_bytes[0] = align_up((size_t)mp[0].splits * L.row_blocks * L.left_blocks * 16 * 128 * 4);
+      lay.counters += (size_t)L.row_blocks * mp[j].n_blocks;
+    } else if (L.exchange) {
       // rows padded to whole row blocks (the fragment layout of the 16- and
       // 32-row tilings stores whole 16-row tiles)
       lay.part_bytes[j] = align_up((size_t)mp[j].splits * (L.row_blocks * 16 * L.m_tiles) * mp[j].w->N * 4);
@@ -418,10 +423,9 @@ int run_group(int32_t n_members, const exl3_weight_t *const *w, const void *x, i
       if ((uintptr_t)y[j] % 2 != 0) return EXL3_EALIGN;
     }
   }
-  if (!ws || !ws->ptr) return EXL3_EWORKSPACE;
-
   const Launch L = choose_launch(mp, n_members, M);
   const Layout lay = layout_for(mp, n_members, M, K, L);
+  if (!ws || !ws->ptr) return EXL3_EWORKSPACE;
   if (lay.counters * 4 > ws->counter_bytes || ws->counter_bytes + lay.rest > ws->bytes) return EXL3_EWORKSPACE;
 
   exl3::RotArgs ra{};

@@ -114,6 +114,10 @@ inline int groups_per_block(int splits, int kernel, bool chained) {
 
 // Launchers (exl3_kernels.hip). Each returns a hipError_t as int.
 int launch_linear(const LinearArgs &a, int bits, int kernel, bool chained, void *stream);
+// The linear launch at BITS bits per weight (exl3_linear_bits.hip, one
+// translation unit per width).
+template <int BITS>
+int launch_linear_bits(const LinearArgs &a, int kernel, bool chained, void *stream);
 int launch_rot(const RotArgs &a, void *stream);
 int launch_dequant(const DequantArgs &a, int bits, void *stream);
 int launch_codebook(const uint16_t *states, uint16_t *out, int64_t n, void *stream);
