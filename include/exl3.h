@@ -68,6 +68,8 @@ extern "C" {
 #define EXL3_EGROUP     (-6)  /* group of 0 or more than 3 members, or members
                                  that differ in K or bits */
 #define EXL3_EHIP       (-7)  /* a HIP launch or call failed */
+#define EXL3_ESCRATCH   (-8)  /* exl3_linear_group_static: the call needs more than
+                                 the library's static scratch */
 
 /* A quantized weight, or a column view of one. Plain descriptor of borrowed
  * device pointers: copying it copies no data. */
@@ -185,6 +187,28 @@ int exl3_rotate(int32_t n_members, const exl3_weight_t *const *w, const void *x,
                 const exl3_workspace_t *ws, void *stream);
 int exl3_linear_rotated(int32_t n_members, const exl3_weight_t *const *w, int64_t M, void *const *y,
                         const int64_t *ldy, const exl3_workspace_t *ws, void *stream);
+
+/* exl3_linear_group_static — exl3_linear_group without a workspace argument,
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation). Its
+ * counters, rotated inputs and split partials live in a static scratch array
+ * of the library: EXL3_STATIC_SCRATCH_BYTES per device (the first
+ * EXL3_STATIC_COUNTER_BYTES of it the split counters), held by every device
+ * the library runs on until the process ends. The first call on a device
+ * resolves that device's copy of the array and zeroes its counter region on
+ * `stream` (a fill kernel, no memset); afterwards each call leaves the
+ * counters at zero, as exl3_linear_group does. The call allocates, frees and
+ * synchronises nothing; it launches the same kernels as exl3_linear_group
+ * and gives the same bytes. Every call on a device shares that device's
+ * scratch: calls that overlap on one GPU (other streams, other threads) race
+ * and must be ordered by the caller. A call that needs more scratch than the
+ * array holds (for example prompt rows: M * K * 2 bytes of rotated input per
+ * member) returns EXL3_ESCRATCH before anything is launched.
+ * Errors: as exl3_linear_group, with ESCRATCH in place of EWORKSPACE. */
+#define EXL3_STATIC_SCRATCH_BYTES (64u << 20)
+#define EXL3_STATIC_COUNTER_BYTES (256u << 10)
+int exl3_linear_group_static(int32_t n_members, const exl3_weight_t *const *w, const void *x,
+                             int64_t ldx, int64_t M, void *const *y, const int64_t *ldy, void *stream);
 
 /* exl3_strerror — static text for an error code. */
 const char *exl3_strerror(int code);

@@ -43,7 +43,7 @@ def fake_weight(K, N, bits, base=0x10000000, block_stride=None):
 def test_exports_every_declared_symbol(lib):
     text = open(ex.HEADER).read()
     names = sorted(set(re.findall(r"^\s*(?:int|const char \*)\s*(exl3_\w+)\s*\(", text, re.M)))
-    assert len(names) == 19
+    assert len(names) == 20
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(ex._SIGNATURES), set(names) ^ set(ex._SIGNATURES)
@@ -411,3 +411,29 @@ def test_synth_is_seeded_and_shaped():
     assert (a.words == b.words).all() and (a.scales == b.scales).all()
     assert a.words.size == 256 * 384 * 3 // 8 and a.scales.size == 384 and a.suh.size == 256
     assert set(a.suh.tolist()) <= {0x3C00, 0xBC00}
+
+
+def test_static_entry_checks_and_mock_launches(lib):
+    """exl3_linear_group_static (the no-allocation variant): the same launches
+    as exl3_linear_group in mock mode, no counter fill per call, and a call
+    too large for the static scratch refused with ESCRATCH before any GPU
+    call (8192 prompt rows of K = 5120: 80 MiB of rotated input)."""
+    import ctypes
+    K = 5120
+    g, u = fake_weight(K, 17408, 4), fake_weight(K, 17408, 4, base=0x20000000)
+    ws_arr = ex._wlist([g, u])
+    ys = (ctypes.c_void_p * 2)(0x30000000, 0x38000000)
+    ld = (ctypes.c_int64 * 2)(17408, 17408)
+    ex.exl3_test_mock(True)
+    for M in (16, 7, 1):
+        assert lib.exl3_linear_group_static(2, ws_arr, 0x40000000, K, M, ys, ld, None) == ex.EXL3_OK
+        launches, fills, _, _ = ex.exl3_test_mock_counts()
+        assert (launches, fills) == (2, 0), M
+    assert lib.exl3_linear_group_static(2, ws_arr, 0x40000000, K, 0, ys, ld, None) == ex.EXL3_OK
+    assert ex.exl3_test_mock_counts()[0] == 0
+    ex.exl3_test_mock(False)
+    # refused on the host: nothing reaches a GPU (there is none here)
+    assert lib.exl3_linear_group_static(2, ws_arr, 0x40000000, K, 8192, ys, ld, None) == ex.EXL3_ESCRATCH
+    assert lib.exl3_linear_group_static(4, ws_arr, 0x40000000, K, 16, ys, ld, None) == ex.EXL3_EGROUP
+    assert lib.exl3_linear_group_static(2, ws_arr, 0, K, 16, ys, ld, None) == ex.EXL3_EINVAL
+    assert b"static scratch" in lib.exl3_strerror(ex.EXL3_ESCRATCH)

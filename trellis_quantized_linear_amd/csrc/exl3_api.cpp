@@ -406,7 +406,8 @@ enum Phase { kRotate = 1, kLinear = 2 };
 // The whole call: checks, plans, workspace layout, then the rotation launch
 // (phase kRotate) and the linear launch (phase kLinear).
 int run_group(int32_t n_members, const exl3_weight_t *const *w, const void *x, int64_t ldx, int64_t M,
-              void *const *y, const int64_t *ldy, const exl3_workspace_t *ws, void *stream, int phases) {
+              void *const *y, const int64_t *ldy, const exl3_workspace_t *ws, void *stream, int phases,
+              bool static_scratch = false) {
   MemberPlan mp[kMaxMembers];
   int e = check_group(n_members, w, M, mp);
   if (e != EXL3_OK) return e;
@@ -425,6 +426,23 @@ int run_group(int32_t n_members, const exl3_weight_t *const *w, const void *x, i
   }
   const Launch L = choose_launch(mp, n_members, M);
   const Layout lay = layout_for(mp, n_members, M, K, L);
+  exl3_workspace_t sws{};
+  if (static_scratch) {
+    // the library's own scratch: refuse what it cannot hold, before any GPU call
+    if (lay.counters * 4 > exl3::kStaticCounterBytes ||
+        exl3::kStaticCounterBytes + lay.rest > exl3::kStaticScratchBytes)
+      return EXL3_ESCRATCH;
+    void *p = (void *)(uintptr_t)0x100000;           // mock mode: never dereferenced
+    if (!g_hooks.mock) {
+      int dev = 0;
+      hipError_t he = hipGetDevice(&dev);
+      if (he != hipSuccess) return hip_fail((int)he);
+      const int se = exl3::static_scratch(dev, stream, &p);
+      if (se != 0) return hip_fail(se);
+    }
+    sws = exl3_workspace_t{p, exl3::kStaticScratchBytes, exl3::kStaticCounterBytes};
+    ws = &sws;
+  }
   if (!ws || !ws->ptr) return EXL3_EWORKSPACE;
   if (lay.counters * 4 > ws->counter_bytes || ws->counter_bytes + lay.rest > ws->bytes) return EXL3_EWORKSPACE;
 
@@ -542,6 +560,11 @@ int exl3_linear_rotated(int32_t n_members, const exl3_weight_t *const *w, int64_
 
 
 
+int exl3_linear_group_static(int32_t n_members, const exl3_weight_t *const *w, const void *x, int64_t ldx,
+                             int64_t M, void *const *y, const int64_t *ldy, void *stream) {
+  return run_group(n_members, w, x, ldx, M, y, ldy, nullptr, stream, kRotate | kLinear, true);
+}
+
 int exl3_linear(const exl3_weight_t *w, const void *x, int64_t ldx, int64_t M, void *y, int64_t ldy,
                 const exl3_workspace_t *ws, void *stream) {
   const exl3_weight_t *ws_[1] = {w};
@@ -560,6 +583,7 @@ const char *exl3_strerror(int code) {
     case EXL3_EWORKSPACE: return "workspace missing or too small for this call";
     case EXL3_EGROUP: return "group must have 1..3 members of one K and one bit width";
     case EXL3_EHIP: return "a HIP launch failed (see exl3_last_hip_error)";
+    case EXL3_ESCRATCH: return "the call needs more than the library's static scratch (64 MiB per device)";
     default: return "unknown error";
   }
 }

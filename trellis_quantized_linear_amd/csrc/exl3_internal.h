@@ -112,6 +112,18 @@ inline int groups_per_block(int splits, int kernel, bool chained) {
   return kernel <= kChain32 ? (splits + waves_per_wg(kernel) - 1) / waves_per_wg(kernel) : splits;
 }
 
+// Static scratch of exl3_linear_group_static: 64 MiB per device, the first
+// 256 KiB of it the counter region.
+constexpr size_t kStaticScratchBytes = size_t(64) << 20;     // EXL3_STATIC_SCRATCH_BYTES
+constexpr size_t kStaticCounterBytes = size_t(256) << 10;    // EXL3_STATIC_COUNTER_BYTES
+constexpr int kMaxDevices = 64;
+
+// The static scratch's device address on device `dev` (the current device):
+// resolved with hipGetSymbolAddress on the first call for that device, which
+// also zeroes its counter region on `stream`; cached afterwards. Returns a
+// hipError_t as int.
+int static_scratch(int dev, void *stream, void **ptr);
+
 // Launchers (exl3_kernels.hip). Each returns a hipError_t as int.
 int launch_linear(const LinearArgs &a, int bits, int kernel, bool chained, void *stream);
 // The linear launch at BITS bits per weight (exl3_linear_bits.hip, one

@@ -7,10 +7,21 @@
 //   fill_zero       zeroes a grown counter region on the caller's stream
 //
 // and the launchers, including the dispatch of a linear launch to its bit
-// width's translation unit.
+// width's translation unit, and the static scratch of
+// exl3_linear_group_static.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "exl3_device.h"
+
+// Scratch of exl3_linear_group_static, for callers that cannot allocate: the
+// split counters (zero at rest) in its first kStaticCounterBytes, then the
+// rotated inputs and split partials of one call. Each device holds its own
+// copy for the life of the process. Host code never uses this name as an
+// address (it is a host-side stand-in there): the device address comes from
+// hipGetSymbolAddress, per device, in static_scratch().
+static __device__ __align__(256) unsigned char scratch[exl3::kStaticScratchBytes];
 
 namespace exl3 {
 namespace {
@@ -136,6 +147,26 @@ int launch_codebook(const uint16_t *states, uint16_t *out, int64_t n, void *stre
   (void)hipGetLastError();
   hipLaunchKernelGGL(codebook_kernel, dim3(wgs), dim3(256), 0, (hipStream_t)stream, states, out, n);
   return (int)hipGetLastError();
+}
+
+int static_scratch(int dev, void *stream, void **ptr) {
+  static std::mutex mu;
+  static void *addr[kMaxDevices] = {};
+  if (dev < 0 || dev >= kMaxDevices) return (int)hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void *p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return (int)e;
+    if (p == nullptr || ((uintptr_t)p & 255) != 0) return (int)hipErrorInvalidSymbol;
+    // the counters must start at zero; afterwards every call's last arrivers
+    // leave them at zero
+    const int f = launch_fill_zero(p, kStaticCounterBytes, stream);
+    if (f != 0) return f;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return 0;
 }
 
 int launch_fill_zero(void *ptr, size_t bytes, void *stream) {

@@ -24,6 +24,9 @@ EXL3_EBITS = -4
 EXL3_EWORKSPACE = -5
 EXL3_EGROUP = -6
 EXL3_EHIP = -7
+EXL3_ESCRATCH = -8
+STATIC_SCRATCH_BYTES = 64 << 20
+STATIC_COUNTER_BYTES = 256 << 10
 WIDE_BLOCKS = 64
 
 
@@ -69,6 +72,7 @@ _SIGNATURES = {
     "exl3_linear": (ctypes.c_int, [W_P, P, I64, I64, P, I64, ctypes.POINTER(exl3_workspace_t), P]),
     "exl3_linear_group": (ctypes.c_int, [I32, ctypes.POINTER(W_P), P, I64, I64, PP, ctypes.POINTER(I64),
                                          ctypes.POINTER(exl3_workspace_t), P]),
+    "exl3_linear_group_static": (ctypes.c_int, [I32, ctypes.POINTER(W_P), P, I64, I64, PP, ctypes.POINTER(I64), P]),
     "exl3_rotate": (ctypes.c_int, [I32, ctypes.POINTER(W_P), P, I64, I64, ctypes.POINTER(exl3_workspace_t), P]),
     "exl3_linear_rotated": (ctypes.c_int, [I32, ctypes.POINTER(W_P), I64, PP, ctypes.POINTER(I64),
                                            ctypes.POINTER(exl3_workspace_t), P]),
@@ -264,6 +268,17 @@ def exl3_linear_group(weights: Sequence[Weight], x, ys, ws: Workspace, stream=No
     ld = (I64 * n)(*[y.stride(0) for y in ys])
     _check(lib().exl3_linear_group(n, _wlist(weights), _ptr(x), x.stride(0), M, yp, ld, ctypes.byref(ws.ws),
                                    _stream_handle(stream)), "exl3_linear_group")
+    return ys
+
+
+def exl3_linear_group_static(weights: Sequence[Weight], x, ys, stream=None, M: Optional[int] = None):
+    """exl3_linear_group in the library's static scratch (no workspace)."""
+    M = x.shape[0] if M is None else M
+    n = len(weights)
+    yp = (ctypes.c_void_p * n)(*[_ptr(y) for y in ys])
+    ld = (I64 * n)(*[y.stride(0) for y in ys])
+    _check(lib().exl3_linear_group_static(n, _wlist(weights), _ptr(x), x.stride(0), M, yp, ld,
+                                          _stream_handle(stream)), "exl3_linear_group_static")
     return ys
 
 
