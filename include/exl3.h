@@ -279,6 +279,15 @@ int exl3_test_fuse_rotation(int32_t on, int32_t spin_limit);
  * planted control "another K split". */
 int exl3_test_force(int32_t m_tiles, int32_t chained, int32_t splits);
 
+/* exl3_test_last_form — the kernel form of the last linear launch the
+ * library issued (or recorded, in mock mode), named as the compiler names
+ * its template instantiation, e.g. "linear_spread_kernel<4>", followed by
+ * " +rot" when the input rotation ran inside it; empty before any launch.
+ * The pages' dispatch test and kernel contract are keyed by these forms
+ * (PR #1467, author follow-up: "A dispatch test"). Errors: EINVAL (buf NULL
+ * or n < 2). */
+int exl3_test_last_form(char *buf, int64_t n);
+
 /* exl3_test_mock — with on != 0, every later device operation (kernel launch,
  * counter fill) is recorded instead of issued, so host logic can be tested
  * without a GPU; exl3_test_mock_counts reads and clears the record. */

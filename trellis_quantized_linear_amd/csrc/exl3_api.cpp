@@ -5,6 +5,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <cstdio>
 #include <cstring>
 
 #include "exl3.h"
@@ -28,6 +29,10 @@ struct TestHooks {
   int64_t fills = 0;
   int64_t fill_bytes = 0;
   void *last_stream = nullptr;
+  // the last linear launch's form (mock or real): bits, kernel, chained,
+  // row blocks, rotation inside the launch
+  int form_bits = 0, form_kernel = -1, form_rows = 0;
+  bool form_chained = false, form_fused = false;
 };
 TestHooks g_hooks;
 
@@ -523,6 +528,13 @@ int run_group(int32_t n_members, const exl3_weight_t *const *w, const void *x, i
     for (int j = 0; j < n_members; ++j) la.m[j].suh = (const uint16_t *)w[j]->suh;
     phases = kLinear;
   }
+  if (phases & kLinear) {
+    g_hooks.form_bits = w[0]->bits;
+    g_hooks.form_kernel = L.kernel;
+    g_hooks.form_chained = L.chained;
+    g_hooks.form_rows = (int)L.row_blocks;
+    g_hooks.form_fused = fuse;
+  }
   if (g_hooks.mock) {
     g_hooks.launches += ((phases & kRotate) ? 1 : 0) + ((phases & kLinear) ? 1 : 0);
     g_hooks.last_stream = stream;
@@ -655,6 +667,20 @@ int exl3_test_force(int32_t m_tiles, int32_t chained, int32_t splits) {
   g_hooks.m_tiles = m_tiles;
   g_hooks.chained = chained;
   g_hooks.splits = splits;
+  return EXL3_OK;
+}
+
+int exl3_test_last_form(char *buf, int64_t n) {
+  if (!buf || n < 2) return EXL3_EINVAL;
+  if (g_hooks.form_kernel < 0) {
+    buf[0] = 0;
+    return EXL3_OK;
+  }
+  exl3::form_name(buf, (size_t)n, g_hooks.form_bits, g_hooks.form_kernel, g_hooks.form_chained, g_hooks.form_rows);
+  if (g_hooks.form_fused) {
+    const size_t len = strlen(buf);
+    snprintf(buf + len, (size_t)n - len, " +rot");
+  }
   return EXL3_OK;
 }
 

@@ -17,6 +17,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <cstdio>
 #include <type_traits>
 
 #include "exl3_internal.h"
@@ -2344,6 +2345,28 @@ LinearFn pick_linear(int kernel, bool chained, int rows) {
   return chained ? pick_kernel<BITS, true>(kernel, rows) : pick_kernel<BITS, false>(kernel, rows);
 }
 
+// The kernel pick_linear returns, named as the compiler names that template
+// instantiation (kStreamOnce = 2, kStreamAgain = 0): the dispatch registry of
+// the tests and the compiler's resource records use these names. Kept beside
+// pick_linear so that the two change together.
+inline void linear_form_name(char *buf, size_t n, int bits, int kernel, bool chained, int rows) {
+  const int pol = rows > 1 ? kStreamAgain : kStreamOnce;
+  const char *ch = chained ? "true" : "false";
+  switch (kernel) {
+    case kSpread16:
+      snprintf(buf, n, rows > 1 ? "linear_spread_rows_kernel<%d>" : "linear_spread_kernel<%d>", bits);
+      return;
+    case kChain16x8: snprintf(buf, n, "linear_chain_kernel<%d, 1, true, 8, 8, %d>", bits, pol); return;
+    case kChain16H: snprintf(buf, n, "linear_chain_kernel<%d, 1, false, 8, 4, %d>", bits, pol); return;
+    case kWide128: snprintf(buf, n, "linear_wide_kernel<%d>", bits); return;
+    case kBlock128: snprintf(buf, n, "linear_block_kernel<%d, %s>", bits, ch); return;
+    case kQuad128: snprintf(buf, n, "linear_quad_kernel<%d>", bits); return;
+    case kChain16: snprintf(buf, n, "linear_chain_kernel<%d, 1, %s, 4, 8, %d>", bits, ch, pol); return;
+    case kChain32: snprintf(buf, n, "linear_chain_kernel<%d, 2, %s, 4, 8, %d>", bits, ch, pol); return;
+    case kNtile64: snprintf(buf, n, "linear_ntile_kernel<%d, 4, %s>", bits, ch); return;
+    default: snprintf(buf, n, "linear_tile_kernel<%d, %s>", bits, ch); return;
+  }
+}
 
 // Launch of the linear kernel `kernel` at BITS bits per weight.
 template <int BITS>

@@ -124,6 +124,10 @@ constexpr int kMaxDevices = 64;
 // hipError_t as int.
 int static_scratch(int dev, void *stream, void **ptr);
 
+// The template instantiation a linear launch of this form runs, as the
+// compiler names it (e.g. "linear_spread_kernel<4>").
+void form_name(char *buf, size_t n, int bits, int kernel, bool chained, int rows);
+
 // Launchers (exl3_kernels.hip). Each returns a hipError_t as int.
 int launch_linear(const LinearArgs &a, int bits, int kernel, bool chained, void *stream);
 // The linear launch at BITS bits per weight (exl3_linear_bits.hip, one

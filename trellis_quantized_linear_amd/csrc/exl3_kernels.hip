@@ -115,6 +115,10 @@ int launch_linear(const LinearArgs &a, int bits, int kernel, bool chained, void 
 }
 
 
+void form_name(char *buf, size_t n, int bits, int kernel, bool chained, int rows) {
+  linear_form_name(buf, n, bits, kernel, chained, rows);
+}
+
 int launch_rot(const RotArgs &a, void *stream) {
   const int64_t items = (int64_t)a.n_members * ((a.M + 3) / 4) * (a.K / 128);
   const int64_t wgs = (items + kWaves - 1) / kWaves;

@@ -84,6 +84,7 @@ _SIGNATURES = {
     "exl3_set_prompt_arithmetic": (ctypes.c_int, [I32]),
     "exl3_test_force": (ctypes.c_int, [I32, I32, I32]),
     "exl3_test_fuse_rotation": (ctypes.c_int, [I32, I32]),
+    "exl3_test_last_form": (ctypes.c_int, [ctypes.c_char_p, I64]),
     "exl3_test_mock": (ctypes.c_int, [I32]),
     "exl3_test_mock_counts": (ctypes.c_int, [ctypes.POINTER(I64), ctypes.POINTER(I64), ctypes.POINTER(I64), PP]),
 }
@@ -332,6 +333,13 @@ def exl3_test_fuse_rotation(on: bool, spin_limit: int = -1):
     default); spin_limit: flag polls before a wave rotates a chunk itself
     (-1: the default)."""
     _check(lib().exl3_test_fuse_rotation(1 if on else 0, spin_limit), "exl3_test_fuse_rotation")
+
+
+def exl3_test_last_form() -> str:
+    """The kernel form of the last linear launch (issued or mock-recorded)."""
+    buf = ctypes.create_string_buffer(128)
+    _check(lib().exl3_test_last_form(buf, 128), "exl3_test_last_form")
+    return buf.value.decode()
 
 
 def exl3_test_mock(on: bool):
