@@ -41,7 +41,7 @@ METRIC = "EXL3 linear weight-stream GB/s at M=1..16; TFLOP/s at M=128 and 8192-r
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA
 NCOPY = 8
-KERNEL_SRC = os.path.join(ROOT, "trellis_quantized_linear_amd", "csrc", "exl3_kernels.hip")
+CSRC = os.path.join(ROOT, "trellis_quantized_linear_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_linear_gate_up_m16.json")
 
 
@@ -260,8 +260,18 @@ def traffic_record():
     if not os.path.exists(TRAFFIC_FILE):
         return None
     rec = json.load(open(TRAFFIC_FILE))
-    cur = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
-    return rec.get("bytes_per_launch") if rec.get("kernel_sha256") == cur else None
+    return rec.get("bytes_per_launch") if rec.get("kernel_sha256") == kernel_source_hash() else None
+
+
+def kernel_source_hash():
+    """sha256 over the device sources (every .hip and .h under csrc, by name):
+    a profile taken on other kernels does not count."""
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".h")):
+            h.update(name.encode())
+            h.update(open(os.path.join(CSRC, name), "rb").read())
+    return h.hexdigest()
 
 
 def main():

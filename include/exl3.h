@@ -263,8 +263,9 @@ int exl3_test_fuse_rotation(int32_t on, int32_t spin_limit);
  * the pages' Linear.min_rows override, PR #1467 follow-up). Neither changes
  * the bits of a row:
  *   m_tiles: -1 automatic, else 1, 2, 4 or 8 16-row MFMA tiles per workgroup,
- *            or 16: 128-row tiles two 128-column blocks wide (the automatic
- *            choice above 128 rows; chained launches only, else as 8);
+ *            or 16: 128-row tiles two 128-column blocks wide (chained
+ *            launches only, else as 8; above 128 rows the automatic choice
+ *            is 8, the 128-row block tiling);
  *   chained: -1 automatic, 0 one K split per workgroup with counter exchange,
  *            1 every split of a block in one workgroup, summed in order,
  *            2 the spread launch (16-row tiles, one S <= 15 for every

@@ -43,9 +43,9 @@ FORMS = {
     "linear_spread_kernel<{b}> +rot": (4, [(256, [34816], 7, "rot")]),
     "linear_spread_rows_kernel<{b}>": (4, [(256, [34816], 17, ""), (256, [17408, 17408], 48, "")]),
     # 128-row tilings
-    "linear_block_kernel<{b}, true>": (2, [(256, [34816], 49, "")]),
+    "linear_block_kernel<{b}, true>": (2, [(256, [34816], 49, ""), (128, [128], 129, ""), (256, [384], 300, ""),
+                                          (256, [1024, 256, 256], 200, "")]),
     "linear_tile_kernel<{b}, false>": (3, [(16384, [128], 97, "")]),
-    "linear_wide_kernel<{b}>": (1, [(128, [128], 129, ""), (256, [384], 300, "")]),
     # opt-in single-chain prompt tiles (other bits than the rest, by design)
     "linear_quad_kernel<{b}>": (1, [(128, [128], 129, "prompt1"), (256, [640], 300, "prompt1")]),
 }
