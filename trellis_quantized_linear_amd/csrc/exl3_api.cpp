@@ -107,6 +107,7 @@ struct Launch {
   int64_t own_blocks = 0;   // spread launch
   int64_t left_blocks = 0;  // spread launch
   bool can_fuse = false;    // the kernel can rotate the input itself (one row block of at most 32 rows)
+  bool fold_launch = false; // 128-row exchanged tiles: the split partials are added by a launch of their own
 };
 
 // CUs of the current device (256 on MI355X; 256 when no device answers).
@@ -262,6 +263,14 @@ Launch choose_launch(const MemberPlan *mp, int n, int64_t M) {
            : !L.chained && long_chains ? exl3::kTile128
                      : exl3::kBlock128;
   L.exchange = !L.chained || (spread && L.left_blocks > 0);
+  // The 2 x 2 tiling's exchange adds 64 KB partials: its last arriving
+  // workgroup would make one memory round trip per split for the whole
+  // block (the down projection at 128 rows: about 22 of its 71 us), while a
+  // launch of 16-row tiles spreads the same additions over the chip. Plans
+  // of up to 16 splits (every automatic plan).
+  int32_t max_splits = 0;
+  for (int j = 0; j < n; ++j) max_splits = std::max(max_splits, mp[j].splits);
+  L.fold_launch = L.kernel == exl3::kTile128 && !L.chained && max_splits <= 16;
   L.can_fuse = L.row_blocks == 1 &&
                (L.kernel == exl3::kSpread16 || L.kernel == exl3::kChain16 || L.kernel == exl3::kChain16H ||
                 L.kernel == exl3::kChain32) &&
@@ -413,7 +422,8 @@ namespace {
 enum Phase { kRotate = 1, kLinear = 2 };
 
 // The whole call: checks, plans, workspace layout, then the rotation launch
-// (phase kRotate) and the linear launch (phase kLinear).
+// (phase kRotate) and the linear launch (phase kLinear; with the split-fold
+// launch after it for 128-row exchanged tiles).
 int run_group(int32_t n_members, const exl3_weight_t *const *w, const void *x, int64_t ldx, int64_t M,
               void *const *y, const int64_t *ldy, const exl3_workspace_t *ws, void *stream, int phases,
               bool static_scratch = false) {
@@ -515,6 +525,7 @@ int run_group(int32_t n_members, const exl3_weight_t *const *w, const void *x, i
                        2 * K * M < (int64_t(1) << 31);
   ra.chunk_major = L.kernel == exl3::kSpread16 || tile_cm ? 1 : 0;
   la.xr_chunk_major = tile_cm ? 1 : 0;
+  la.fold_launch = L.fold_launch ? 1 : 0;
   la.n_members = n_members;
   la.M = (int32_t)M;
   la.K = (int32_t)K;
@@ -540,7 +551,7 @@ int run_group(int32_t n_members, const exl3_weight_t *const *w, const void *x, i
     g_hooks.form_fused = fuse;
   }
   if (g_hooks.mock) {
-    g_hooks.launches += ((phases & kRotate) ? 1 : 0) + ((phases & kLinear) ? 1 : 0);
+    g_hooks.launches += ((phases & kRotate) ? 1 : 0) + ((phases & kLinear) ? (L.fold_launch ? 2 : 1) : 0);
     g_hooks.last_stream = stream;
     return EXL3_OK;
   }
@@ -551,6 +562,10 @@ int run_group(int32_t n_members, const exl3_weight_t *const *w, const void *x, i
   if (phases & kLinear) {
     e = exl3::launch_linear(la, w[0]->bits, L.kernel, L.chained, stream);
     if (e) return hip_fail(e);
+    if (L.fold_launch) {
+      e = exl3::launch_split_fold(la, stream);
+      if (e) return hip_fail(e);
+    }
   }
   return EXL3_OK;
 }

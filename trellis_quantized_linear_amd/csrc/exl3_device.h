@@ -1516,6 +1516,7 @@ void linear_tile_kernel(const LinearArgs a) {
           __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[mt][i2]), rp,
                                                  ((4 * wr + mt) * 8 + 4 * wc + i2) * 1024 + 16 * lane, 0,
                                                  kAgentScope);
+    if (a.fold_launch) return;                             // the split-fold launch adds them (uniform)
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
     __shared__ int s_last;

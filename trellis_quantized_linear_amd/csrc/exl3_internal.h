@@ -45,6 +45,8 @@ struct LinearArgs {
   int32_t own_blocks;         // spread launch: blocks owned by one workgroup each (= total_wgs)
   int32_t left_blocks;        // spread launch: blocks whose splits go to spare waves
   int32_t xr_chunk_major;     // 128-row tilings: Xr is chunk-major (else row-major)
+  int32_t fold_launch;        // 128-row exchanged tiles: store the split partials only; a split-fold
+                              // launch adds them and finishes the rows
   // Fused input rotation (decode and 32-row launches): the launch itself
   // writes every member's Xr from x before its chains read it. sync[0]
   // counts finished workgroups; sync[1 + j * K/128 + k] says that member j's
@@ -55,6 +57,14 @@ struct LinearArgs {
   uint32_t *sync;
   int32_t spin_limit;         // polls of an unwritten chunk's flag before a wave rotates it itself
 };
+
+// Workgroups of the split-fold launch that follows a 128-row exchanged
+// launch: one per (member, row block, block, 16-row tile).
+inline int64_t split_fold_wgs(const LinearArgs &a) {
+  int64_t n = 0;
+  for (int j = 0; j < a.n_members; ++j) n += (int64_t)a.row_blocks * a.m[j].n_blocks * 8;
+  return n;
+}
 
 // Words of the sync region of a fused launch.
 inline int64_t fused_sync_words(int n_members, int64_t K) { return 1 + (int64_t)n_members * (K / 128); }
@@ -135,6 +145,8 @@ int launch_linear(const LinearArgs &a, int bits, int kernel, bool chained, void 
 template <int BITS>
 int launch_linear_bits(const LinearArgs &a, int kernel, bool chained, void *stream);
 int launch_rot(const RotArgs &a, void *stream);
+// The split-fold launch after a linear launch with fold_launch set.
+int launch_split_fold(const LinearArgs &a, void *stream);
 int launch_dequant(const DequantArgs &a, int bits, void *stream);
 int launch_codebook(const uint16_t *states, uint16_t *out, int64_t n, void *stream);
 int launch_fill_zero(void *ptr, size_t bytes, void *stream);

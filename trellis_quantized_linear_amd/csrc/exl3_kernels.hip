@@ -5,6 +5,8 @@
 //   dequant_kernel  test hook: the decoded weights, through the same decoder
 //   codebook_kernel test hook: the codebook on arbitrary states
 //   fill_zero       zeroes a grown counter region on the caller's stream
+//   split_fold      adds the split partials of a 128-row exchanged launch
+//                   and finishes its rows
 //
 // and the launchers, including the dispatch of a linear launch to its bit
 // width's translation unit, and the static scratch of
@@ -46,6 +48,70 @@ __global__ __launch_bounds__(kThreads) void rot_kernel(const RotArgs a) {
   const u32x4 out = rot_lane(load8_u16(a.x + (int64_t)row * a.ldx + k0), load8_u16(suh + k0), c, a.natural_order != 0);
   const int64_t at = a.chunk_major ? ((int64_t)(k0 >> 5) * a.M + row) * 32 + (k0 & 31) : (int64_t)row * a.K + k0;
   *(u32x4 *)(xr + at) = out;
+}
+
+// ------------------------------------------------------------ split fold
+//
+// After a 128-row exchanged launch that only stored its split partials
+// (LinearArgs::fold_launch): one workgroup per (member, row block, block,
+// 16-row tile) adds that tile's S partials in split order, z = P0, then
+// z + P1, ... (the same fp32 additions, in the same order, as the linear
+// launch's last arriving workgroup would make), and runs the epilogue of its
+// 16 rows. A tile is 16 rows x 128 columns, 8 KB per split in the fragment
+// layout; thread x owns fragments x and x + 256 of its 512 and issues the
+// loads of every split before the first addition.
+__global__ __launch_bounds__(kThreads) void split_fold_kernel(const LinearArgs a) {
+  constexpr int kMaxSplits = 16;
+  const int RB = a.row_blocks;
+  int64_t local = blockIdx.x;
+  int j = 0;
+  while (j + 1 < a.n_members && local >= (int64_t)RB * a.m[j].n_blocks * 8) {
+    local -= (int64_t)RB * a.m[j].n_blocks * 8;
+    ++j;
+  }
+  const MemberArgs &m = a.m[j];
+  const int per_rb = m.n_blocks * 8;
+  const int rb = (int)(local / per_rb);
+  const int rem = (int)(local - (int64_t)rb * per_rb);
+  const int nb = rem >> 3, mt = rem & 7;
+  const int row0 = 128 * rb + 16 * mt;
+  if (row0 >= a.M) return;                                 // uniform
+  const int S = m.splits;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int col0 = nb * kBlockCols;
+
+  u32x4 v[kMaxSplits][2];
+#pragma unroll
+  for (int s = 0; s < kMaxSplits; ++s) {
+    if (s < S) {                                           // uniform
+      const __amdgpu_buffer_rsrc_t rp = make_rsrc(partial_frag(m, s, rb, nb, RB, 8) + mt * 8 * 256, 8 * 1024);
+#pragma unroll
+      for (int e = 0; e < 2; ++e)
+        v[s][e] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                rp, 16 * (int)(threadIdx.x + e * kThreads), 0, kAgentScope));
+    }
+  }
+  f32x4 z[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) z[e] = __builtin_bit_cast(f32x4, v[0][e]);
+#pragma unroll
+  for (int s = 1; s < kMaxSplits; ++s)
+    if (s < S)
+#pragma unroll
+      for (int e = 0; e < 2; ++e) z[e] = z[e] + __builtin_bit_cast(f32x4, v[s][e]);
+
+  __shared__ __attribute__((aligned(16))) float zrow[16 * 132];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int f = threadIdx.x + e * kThreads;              // column tile f / 64, lane f % 64
+    const int fl = f & 63, ft = f >> 6;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) zrow[(4 * (fl >> 4) + q) * 132 + 16 * ft + (fl & 15)] = z[e][q];
+  }
+  const EpiCols ec = epi_cols(m, col0, lane);
+  __syncthreads();
+  if (row0 + 4 * wave < a.M) epilogue_rows_lds<1>(zrow + 4 * wave * 132, 132, ec, lane, m, col0, row0 + 4 * wave, a.M);
 }
 
 // ------------------------------------------------------------ test hooks
@@ -124,6 +190,16 @@ int launch_rot(const RotArgs &a, void *stream) {
   const int64_t wgs = (items + kWaves - 1) / kWaves;
   (void)hipGetLastError();
   hipLaunchKernelGGL(rot_kernel, dim3((unsigned)wgs), dim3(kThreads), 0, (hipStream_t)stream, a);
+  return (int)hipGetLastError();
+}
+
+int launch_split_fold(const LinearArgs &a, void *stream) {
+  const int64_t wgs = split_fold_wgs(a);
+  for (int j = 0; j < a.n_members; ++j)
+    if (a.m[j].splits < 1 || a.m[j].splits > 16) return (int)hipErrorInvalidValue;
+  if (wgs <= 0 || wgs >= (int64_t(1) << 31)) return (int)hipErrorInvalidValue;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(split_fold_kernel, dim3((unsigned)wgs), dim3(kThreads), 0, (hipStream_t)stream, a);
   return (int)hipGetLastError();
 }
 
