@@ -509,6 +509,9 @@ def run_extras(ex, torch, synth, layers, copies, only=None):
     return run_extras_prefill(ex, torch, synth, copies, extra, only)
 
 
+PREFILL_WARM, PREFILL_REPS = 30, 20
+
+
 def run_extras_prefill(ex, torch, synth, copies, extra, only):
     K = synth.HIDDEN
     if only not in (None, "prefill"):
@@ -524,8 +527,11 @@ def run_extras_prefill(ex, torch, synth, copies, extra, only):
     wsc = ex.Workspace().reserve([down], m)
     ga, gb, gc = Group(ex, six[:3], xa, m, wsa), Group(ex, six[3:], xa, m, wsb), Group(ex, [down], xb, m, wsc)
     fn = lambda: (ga.call(), gb.call(), gc.call())
-    fn()
-    ms = time_events(fn, 3)
+    # a prompt runs layer after layer: these launches run power-limited, so
+    # each figure is taken at the steady clock, after 30 layers of the same
+    # work (a few-layer window right after other work reads up to 10 % off)
+    time_events(fn, PREFILL_WARM)
+    ms = time_events(fn, PREFILL_REPS)
     fl = flops(six + [down], m)
     extra["prefill_8192_TFLOPs"] = round(fl / (ms * 1e-3) / 1e12, 1)
     extra["prefill_8192_ms_per_layer"] = round(ms, 3)
@@ -535,14 +541,24 @@ def run_extras_prefill(ex, torch, synth, copies, extra, only):
     # bits than every other regime; exl3_set_prompt_arithmetic(1))
     ex.exl3_set_prompt_arithmetic(1)
     try:
-        fn()
-        ms1 = time_events(fn, 3)
+        time_events(fn, PREFILL_WARM)
+        ms1 = time_events(fn, PREFILL_REPS)
     finally:
         ex.exl3_set_prompt_arithmetic(0)
     extra["prefill_8192_single_chain_opt_in_TFLOPs"] = round(fl / (ms1 * 1e-3) / 1e12, 1)
     extra["prefill_8192_single_chain_opt_in_ms_per_layer"] = round(ms1, 3)
     log(f"prefill 8192 rows, opt-in single chain: {ms1:.2f} ms per layer, "
         f"{extra['prefill_8192_single_chain_opt_in_TFLOPs']} TFLOP/s")
+    # the same bits on the 128 x 256 tiling (one workgroup of two blocks per
+    # CU), which the automatic choice passes over for the 128-row block tiling
+    ex.exl3_test_force(16, 1, 0)
+    try:
+        time_events(fn, PREFILL_WARM)
+        ms2 = time_events(fn, PREFILL_REPS)
+    finally:
+        ex.exl3_test_force(-1, -1, 0)
+    extra["prefill_8192_tiling_128x256_ms_per_layer"] = round(ms2, 3)
+    log(f"prefill 8192 rows, 128 x 256 tiling (same bits): {ms2:.2f} ms per layer")
     del ga, gb, gc, xa, xb, wsa, wsb, wsc
     return run_extras_head(ex, torch, synth, extra, only)
 

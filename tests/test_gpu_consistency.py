@@ -338,3 +338,29 @@ def test_spread_launch_over_several_row_blocks():
             other = [G.host_u16(y) for y in G.run_group(ws_, xd, M=M, ws=ws, tag=f"forced {force}")]
             ex().exl3_test_force(-1, -1, 0)
             assert all(np.array_equal(a, b) for a, b in zip(auto, other)), (M, force)
+
+
+def test_split_fold_launch_equals_the_chained_fold():
+    """Down-shaped weight (K 17408: long splits) at 100 and 128 rows: the
+    exchanged 2 x 2 tiling whose partials the split-fold launch adds gives
+    the bytes of the chained 128-row block tiling (every split folded in one
+    workgroup); with a forced plan of 17 splits the tiling folds in its last
+    arriving workgroup instead, again byte for byte the chained form.
+    Counters zero afterwards."""
+    K, N = 17408, 1024
+    L = G.layer("split-fold", "down", K, N, 4)
+    w = G.upload(L)
+    xd = G.dev_bf16(G.xbits("split-fold", 128, K))
+    ws = ex().Workspace().reserve([w], 128)
+    for M in (100, 128):
+        for S in (0, 17):
+            ys = {}
+            for chained in (0, 1):
+                ex().exl3_test_force(8, chained, S)
+                ws.reserve([w], M)
+                ys[chained] = G.host_u16(G.run(w, xd, M=M, ws=ws, tag=f"split fold M={M} S={S} chained={chained}"))
+                form = ex().exl3_test_last_form()
+                ex().exl3_test_force(-1, -1, 0)
+                assert form == ("linear_tile_kernel<4, false>" if chained == 0 else "linear_block_kernel<4, true>"), form
+            assert np.array_equal(ys[0], ys[1]), (M, S)
+            assert int(ws.counters().abs().sum()) == 0, (M, S)

@@ -187,12 +187,13 @@ Launch choose_launch(const MemberPlan *mp, int n, int64_t M) {
     }
   }
   int mt = g_hooks.m_tiles;
-  // 16: 128-row tiles two blocks wide (forced only: above 128 rows the
-  // block tiling, two workgroups of 128 rows x one block per CU, measured
-  // faster at 8192 prompt rows on every projection of the 27B layer:
-  // {gate, up} 2975-2995 against 3106-3364 us, {q, k, v} 866 against 915,
-  // down 1614 against 1630)
-  const bool wide = mt == 16;
+  // 16: 128-row tiles two blocks wide. Automatic above 128 rows for long
+  // splits (down): at the steady clock of a long prompt (these launches run
+  // power-limited) the 8192-row down projection took 1260 us against 1333
+  // on the block tiling (two workgroups of 128 rows x one block per CU),
+  // which stays for the rest ({gate, up} 2913 against 2944 us, {q, k, v}
+  // 711 against 709); the same bits either way.
+  const bool wide = mt == 16 || (mt == -1 && M > 128 && long_chains);
   int mid_chained = -1;
   bool mid_spread = false;
   if (mt == 16) {
