@@ -27,7 +27,8 @@
  *     sums are fp32 in one canonical order, outputs are bf16. Row m of Y is
  *     byte-identical for every row count M, every row regime, group
  *     membership and column view (TensorFold PR #1467, "The arithmetic";
- *     PR #1407, review item 1: a prompt row's bits equal its decode-row bits).
+ *     PR #1407, review item 1: a row gives the same bytes in a prompt call as
+ *     in a decode call).
  *
  * Formats (all little-endian):
  *   packed words  block-major: the 16x16 tile at column block nb, tile row kt,
@@ -166,8 +167,7 @@ int exl3_linear(const exl3_weight_t *w, const void *x, int64_t ldx, int64_t M,
 
 /* exl3_linear_group — up to three members of one K and one bits over the same
  * X in one rotation launch and one linear launch (PR #1467, "What this
- * changes": up to three layers of one K over the same rows in one rotation
- * and one launch). Each member keeps its own plan, suh, scales and svh, and
+ * changes"). Each member keeps its own plan, suh, scales and svh, and
  * its output y[j] (ldy[j]) is byte-identical to exl3_linear of that member
  * alone. Errors: as exl3_linear, plus EGROUP. */
 int exl3_linear_group(int32_t n_members, const exl3_weight_t *const *w, const void *x,

@@ -5,9 +5,9 @@ occupancy its launch was designed for.
 
 The pages require the same of their kernels (TensorFold PR #1467, "Receipt",
 "Kernel contract": every launch registered in gates 1-4, with a resource
-record; author follow-up, "A dispatch test": a host sweep over K and N up to
-16384 fails on any form the dispatch reaches that no registration's gate
-shapes run). Here a form is a kernel template instantiation, named as the
+record; author follow-up, "A dispatch test": a host-side sweep of the
+dispatch over K and N up to 16384 must find each reachable form among the
+registered ones, each run by some gate shape). Here a form is a kernel template instantiation, named as the
 compiler names it (exl3_test_last_form, the build's resource records).
 
 A gate is (K, [N of each member], M, mode): mode "" is the automatic

@@ -379,9 +379,8 @@ def check_special_values_propagate():
 
 
 def check_rows_independent():
-    """Row independence, the pages' "window outputs equal step outputs"
-    (TensorFold PR #1467, "Receipt": window logits equal step logits byte for
-    byte): the oracle at M = 7 rows gives, row for row, the bytes of seven
+    """Row independence (TensorFold PR #1467, "Receipt": a window of rows and
+    one-row steps give identical bytes): the oracle at M = 7 rows gives, row for row, the bytes of seven
     one-row calls, and the rows of a column view those of the full weight's
     columns (K = 256, N = 384, 3 bits)."""
     from trellis_quantized_linear_amd import synth

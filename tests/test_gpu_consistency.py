@@ -1,8 +1,8 @@
 """GPU self-consistency, bitwise: a row's bytes do not depend on how many rows
 are in the call, on the row tiling or launch shape, on group membership or on
 column views (TensorFold PR #1467 "The arithmetic" and its gate 3; PR #1407
-review item 1; PR #1507 review: views plan as the whole head does, so the
-logits keep their bits). Counters are zero whenever no call runs (PR #1475).
+review item 1; PR #1507 review: a wide view takes the full head's plan, so
+its logits keep their bytes). Counters are zero whenever no call runs (PR #1475).
 
 Planted controls (another K split, a member's scales swapped, a member's suh
 swapped) must change bytes, which shows the comparisons can see a change.
@@ -119,9 +119,9 @@ def test_prompt_rows_equal_decode_rows():
 
 @pytest.mark.parametrize("M", [1, 7, 16, 200])
 def test_group_equals_each_member_alone(M):
-    """PR #1467 exl3-midm: the q/k/v and gate/up groups equal each member's own
-    launch at 1, 7 and 16 rows, and at 200 prompt rows (two row blocks, the
-    members' tiles side by side in one launch)."""
+    """PR #1467 exl3-midm: a {q, k, v} or {gate, up} group call gives, per
+    member, the bytes of that member's solo call, at 1, 7, 16 and 200 prompt
+    rows (two row blocks, the members' tiles side by side in one launch)."""
     K = synth.HIDDEN
     x = G.xbits("group", M, K)
     xd = G.dev_bf16(x)
@@ -137,8 +137,8 @@ def test_group_equals_each_member_alone(M):
 
 
 def test_group_planted_controls():
-    """Planted controls: a group with one member's scales swapped, and one with
-    one member's suh swapped, must change that member's bytes."""
+    """Planted controls: exchanging the scales (then the suh) of one group
+    member for another's must change that member's bytes."""
     K, M = 5120, 7
     x = G.dev_bf16(G.xbits("control", M, K))
     a = G.layer("control", "a", K, 1024, 4)

@@ -1,6 +1,6 @@
-"""Float64 error report: the "a changed reduction order keeps native error no
-worse" criterion of the pages' review of the mid-M path (PR #1467, review
-item 1, "Fixed plans": only plans that are no worse at both 16 and 128 rows).
+"""Float64 error report: the pages' rule for the mid-M path that a new
+summation order may not raise the error against float64 (PR #1467, review
+item 1, "Fixed plans"), checked at 16 rows and again at 128 rows.
 
 For several shapes, every K-split count tried (the plan's and forced others)
 runs at 16 and at 128 rows. Each GPU Y is compared with the exact result

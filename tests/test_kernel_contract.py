@@ -5,11 +5,11 @@ registered form (TensorFold PR #1467, author follow-up, "A dispatch test";
 record).
 
 * The sweep calls the library's dispatch (mock mode: launches are recorded,
-  not issued) over K and N from 128 to 16384 (and the 27B's 17408 and
+  not issued) over K, N in 128..16384 (and the 27B's 17408 and
   248,320), 1 to 128 rows and the prompt rows 129, 200, 300 and 8192, for
   single weights and for groups of two and three members, in the default
   mode, the opt-in prompt arithmetic and with the in-launch rotation. It
-  fails on any form that no registration names; the planted control removes
+  fails when it reaches a form the registry lacks; the planted control removes
   one registration and must see the sweep fail on it.
 * Every registered gate shape, at every width, must reach its form.
 * The build's resource records (kernel_resources.json, from the compiler's

@@ -388,8 +388,8 @@ def test_test_force_validation(lib):
 
 
 def test_dispatch_sweep_reaches_only_built_forms(lib):
-    """The pages' dispatch sweep (PR #1467 follow-up): K and N from 128 to
-    16384 at 1..128 rows through the host dispatch; every call must be
+    """The pages' dispatch sweep (PR #1467 follow-up): K, N in 128..16384 at
+    1..128 rows through the host dispatch; every call must be
     accepted (the kernel table covers every width x row tiling x launch
     shape), with a workspace sized by exl3_workspace_need."""
     ex.exl3_test_mock(True)
