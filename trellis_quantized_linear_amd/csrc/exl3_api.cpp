@@ -152,10 +152,12 @@ MidChoice mid_m_choice(int64_t blocks, bool long_chains, int64_t M) {
   const int64_t w16 = blocks * ((M + 15) / 16);            // workgroups of the chained 16-row form
   if (blocks >= 128) return w16 <= 1024 ? MidChoice{1, true} : MidChoice{8, true};
   if (!long_chains) return M <= 32 ? MidChoice{1, false} : MidChoice{1, true};
-  // few blocks, long splits (down): the exchange keeps the CUs busy
+  // few blocks, long splits (down): the exchange keeps the CUs busy; from
+  // 49 rows on the 128-row exchanged tiles with the split-fold launch (down
+  // at 49, 64, 80 and 96 rows 41-44 us against 45-53 us for the chained
+  // 16-row form)
   if (M <= 32) return {2, false};
   if (M <= 48) return {1, false};
-  if (M <= 96) return {1, true};
   return {8, false};
 }
 
