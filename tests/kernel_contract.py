@@ -45,7 +45,7 @@ FORMS = {
     # 128-row tilings
     "linear_block_kernel<{b}, true>": (2, [(256, [34816], 49, ""), (128, [128], 129, ""), (256, [384], 300, ""),
                                           (256, [1024, 256, 256], 200, "")]),
-    "linear_tile_kernel<{b}, false>": (3, [(16384, [128], 97, "")]),
+    "linear_tile_kernel<{b}, false>": (3, [(16384, [128], 97, ""), (16384, [128, 256], 64, "")]),
     # prompt rows of long-split weights (down): 128 rows x 2 blocks (the last pair of an odd count: 1)
     "linear_wide_kernel<{b}>": (1, [(16384, [128], 129, ""), (16384, [384], 300, ""), (17408, [256, 128], 200, "")]),
     # opt-in single-chain prompt tiles (other bits than the rest, by design)
