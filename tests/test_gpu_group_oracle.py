@@ -11,7 +11,11 @@ output is its own single-weight launch's, which the oracle defines).
   compared with the oracle, beside the first, last and a random block of
   each member.
 * The 3-bit {gate, up} pair of the 3.5 bpw MLP at 17, 32 and 48 rows: the
-  spread launch over several 16-row blocks in one grid.
+  spread launch over several 16-row blocks in one grid; at 49, 100 and 128
+  rows the chained 128-row block tiling with one workgroup per CU, the
+  blocks past one per CU split one chain to a workgroup and finished by the
+  split-fold launch (every such block against the oracle, and rows 0 and
+  M - 1 byte for byte against one-row calls).
 * A stress of the relaxed split-K exchange on that headline launch: 10^4
   group calls at 16 rows, bytes compared every 100 calls, counters zero at
   the end (PR #1475, "What this changes": the last arriver resets its
@@ -92,6 +96,21 @@ def test_gate_up_3bit_spread_over_row_blocks_vs_oracle(M):
     """The 3.5 bpw MLP's {gate, up} pair at mid rows: the spread launch once
     per 16-row block in one grid, left blocks per row block."""
     check_group(("gate", "up"), M, 3, "group-oracle-c3", "x")
+
+
+@pytest.mark.parametrize("M", [49, 100, 128])
+def test_gate_up_3bit_block_tiling_left_blocks_vs_oracle(M):
+    """The 3.5 bpw MLP's {gate, up} pair at 49-128 rows: 256 block workgroups,
+    the 16 left blocks' splits one per workgroup after its own block."""
+    check_group(("gate", "up"), M, 3, "group-oracle-c3", "x")
+    layers = [G.layer("group-oracle-c3", n, K, COLS[n], 3) for n in ("gate", "up")]
+    ws_ = [G.upload(L) for L in layers]
+    xd = G.dev_bf16(G.xbits("group-oracle-c3", M, K, tag="x"))
+    full = [G.host_u16(y) for y in G.run_group(ws_, xd, M=M, tag=f"left blocks M={M}")]
+    for r in sorted({0, M - 1}):
+        one = [G.host_u16(y) for y in G.run_group(ws_, xd[r:r + 1], M=1, tag=f"row {r} alone")]
+        for j in range(2):
+            assert np.array_equal(one[j][0], full[j][r]), (M, r, j)
 
 
 def test_gate_up_spread_exchange_stress():

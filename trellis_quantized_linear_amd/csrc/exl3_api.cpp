@@ -108,6 +108,8 @@ struct Launch {
   int64_t left_blocks = 0;  // spread launch
   bool can_fuse = false;    // the kernel can rotate the input itself (one row block of at most 32 rows)
   bool fold_launch = false; // 128-row exchanged tiles: the split partials are added by a launch of their own
+  bool block_left = false;  // chained 128-row blocks, one row block: own_blocks workgroups, left blocks' splits
+                            // one per workgroup after its own block, added by the split-fold launch
 };
 
 // CUs of the current device (256 on MI355X; 256 when no device answers).
@@ -274,6 +276,20 @@ Launch choose_launch(const MemberPlan *mp, int n, int64_t M) {
   int32_t max_splits = 0;
   for (int j = 0; j < n; ++j) max_splits = std::max(max_splits, mp[j].splits);
   L.fold_launch = L.kernel == exl3::kTile128 && !L.chained && max_splits <= 16;
+  // The chained 128-row block tiling over one row block with a few more
+  // blocks than CUs ({gate, up} at 49-128 rows: 272 blocks on 256 CUs): the
+  // blocks past one per CU would run as second workgroups on a few CUs and
+  // set the launch time; instead each CU's workgroup runs one split of one
+  // of them after its own block, and the split-fold launch adds those
+  // partials. Every member with one plan S.
+  bool one_plan = true;
+  for (int j = 1; j < n; ++j) one_plan = one_plan && mp[j].splits == mp[0].splits;
+  if (L.kernel == exl3::kBlock128 && L.chained && L.row_blocks == 1 && one_plan && mp[0].splits <= 16 &&
+      blocks > ncu && (blocks - ncu) * mp[0].splits <= ncu) {
+    L.block_left = true;
+    L.own_blocks = ncu;
+    L.left_blocks = blocks - ncu;
+  }
   L.can_fuse = L.row_blocks == 1 &&
                (L.kernel == exl3::kSpread16 || L.kernel == exl3::kChain16 || L.kernel == exl3::kChain16H ||
                 L.kernel == exl3::kChain32) &&
@@ -291,6 +307,7 @@ struct Layout {
 
 Layout layout_for(const MemberPlan *mp, int n, int64_t M, int64_t K, const Launch &L) {
   Layout lay{};
+  int64_t first_block = 0;   // the member's first block among the launch's blocks
   for (int j = 0; j < n; ++j) {
     lay.xr_bytes[j] = align_up((size_t)M * K * 2);
     if (L.exchange && L.kernel == exl3::kSpread16) {
@@ -303,7 +320,12 @@ Layout layout_for(const MemberPlan *mp, int n, int64_t M, int64_t K, const Launc
       // 32-row tilings stores whole 16-row tiles)
       lay.part_bytes[j] = align_up((size_t)mp[j].splits * (L.row_blocks * 16 * L.m_tiles) * mp[j].w->N * 4);
       lay.counters += (size_t)L.row_blocks * mp[j].n_blocks;
+    } else if (L.block_left) {
+      // the member's left blocks (those past own_blocks): [split][left block] x 128 x 128 floats
+      const int64_t left = std::max<int64_t>(0, std::min<int64_t>(mp[j].n_blocks, first_block + mp[j].n_blocks - L.own_blocks));
+      lay.part_bytes[j] = align_up((size_t)mp[j].splits * left * 128 * 128 * 4);
     }
+    first_block += mp[j].n_blocks;
     lay.rest += lay.xr_bytes[j] + lay.part_bytes[j];
   }
   lay.sync_at = lay.counters;
@@ -500,12 +522,16 @@ int run_group(int32_t n_members, const exl3_weight_t *const *w, const void *x, i
       off += lay.part_bytes[j];
       m.counters = (uint32_t *)base + counter_off;
       counter_off += (size_t)L.row_blocks * mp[j].n_blocks;
+    } else if (L.block_left) {
+      m.partials = (float *)(base + off);
+      off += lay.part_bytes[j];
     }
     wg += L.kernel == exl3::kWide128   ? L.row_blocks * ((mp[j].n_blocks + 1) / 2)
         : L.kernel == exl3::kQuad128 ? L.row_blocks * ((mp[j].n_blocks + 3) / 4)
                                      : L.row_blocks * mp[j].n_blocks * m.groups;
   }
   if (L.kernel == exl3::kSpread16) wg = L.row_blocks * L.own_blocks;
+  if (L.block_left) wg = L.own_blocks;
   if (wg >= (int64_t(1) << 31)) return EXL3_EINVAL;
   la.own_blocks = (int32_t)L.own_blocks;
   la.left_blocks = (int32_t)L.left_blocks;
@@ -554,7 +580,7 @@ int run_group(int32_t n_members, const exl3_weight_t *const *w, const void *x, i
     g_hooks.form_fused = fuse;
   }
   if (g_hooks.mock) {
-    g_hooks.launches += ((phases & kRotate) ? 1 : 0) + ((phases & kLinear) ? (L.fold_launch ? 2 : 1) : 0);
+    g_hooks.launches += ((phases & kRotate) ? 1 : 0) + ((phases & kLinear) ? (L.fold_launch || L.block_left ? 2 : 1) : 0);
     g_hooks.last_stream = stream;
     return EXL3_OK;
   }
@@ -567,6 +593,28 @@ int run_group(int32_t n_members, const exl3_weight_t *const *w, const void *x, i
     if (e) return hip_fail(e);
     if (L.fold_launch) {
       e = exl3::launch_split_fold(la, stream);
+      if (e) return hip_fail(e);
+    }
+    if (L.block_left) {
+      // the split-fold launch over the left blocks only: each member that
+      // has some, its pointers moved to its first left block
+      exl3::LinearArgs fa = la;
+      int nf = 0;
+      int64_t first_block = 0;
+      for (int j = 0; j < n_members; ++j) {
+        const int64_t fl = std::max<int64_t>(0, L.own_blocks - first_block);
+        if (fl < mp[j].n_blocks) {
+          exl3::MemberArgs f = la.m[j];
+          f.scales += fl * kBlockCols;
+          f.svh += fl * kBlockCols;
+          f.y += fl * kBlockCols;
+          f.n_blocks = (int32_t)(mp[j].n_blocks - fl);
+          fa.m[nf++] = f;
+        }
+        first_block += mp[j].n_blocks;
+      }
+      fa.n_members = nf;
+      e = exl3::launch_split_fold(fa, stream);
       if (e) return hip_fail(e);
     }
   }

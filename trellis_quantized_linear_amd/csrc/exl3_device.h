@@ -1915,9 +1915,11 @@ void linear_block_kernel(const LinearArgs a) {
   // copies: wave w moves input operands 2w + e (lane l brings row
   // 16 (2w + e) + l % 16, 16-byte column l / 16) and half w % 2 of tile row
   // w / 2 of every chunk
-  const __amdgpu_buffer_rsrc_t ra =
-      a.xr_chunk_major ? make_rsrc(m.xr + (int64_t)row_base * kChunk, (uint32_t)(C * M - row_base) * 64u)
-                       : make_rsrc(m.xr + (int64_t)row_base * K, (uint32_t)min(M - row_base, 128) * (uint32_t)K * 2u);
+  auto xr_rsrc = [&](const MemberArgs &mm) {
+    return a.xr_chunk_major ? make_rsrc(mm.xr + (int64_t)row_base * kChunk, (uint32_t)(C * M - row_base) * 64u)
+                            : make_rsrc(mm.xr + (int64_t)row_base * K, (uint32_t)min(M - row_base, 128) * (uint32_t)K * 2u);
+  };
+  __amdgpu_buffer_rsrc_t ra = xr_rsrc(m);
   // Xr chunk-major (each chunk's M rows contiguous, 64 bytes a row) or row-major
   const int a_row = a.xr_chunk_major ? 64 : 2 * K;           // bytes from one row to the next
   const int a_step = a.xr_chunk_major ? 64 * M : 64;         // bytes from one chunk to the next
@@ -1927,7 +1929,7 @@ void linear_block_kernel(const LinearArgs a) {
     const int r = 16 * (2 * wave + e) + c;
     va[e] = row_base + r < M ? (uint32_t)(r * a_row + 16 * g) : kOutOfRange;
   }
-  const __amdgpu_buffer_rsrc_t rw = make_rsrc(m.words + (int64_t)nb * m.block_stride, (uint32_t)m.block_stride);
+  __amdgpu_buffer_rsrc_t rw = make_rsrc(m.words + (int64_t)nb * m.block_stride, (uint32_t)m.block_stride);
   const int hrow = wave >> 1, half = wave & 1;
   const uint32_t vw =
       16 * lane < BL::kPiece ? (uint32_t)(hrow * BL::kRowBytes + half * BL::kPiece + 16 * lane) : kOutOfRange;
@@ -1963,7 +1965,7 @@ void linear_block_kernel(const LinearArgs a) {
   // chunk range: every split (chained) or split sg
   const int cbeg = CHAINED ? 0 : (int)(sg * C / S);
   const int cend = CHAINED ? C : (int)((sg + 1) * C / S);
-  const int last = cend - 1;
+  int last = cend - 1;
 
   // z = P0 + P1 + ... in split order, starting from +0: an MFMA chain that
   // starts from +0 never ends in -0, so +0 + P0 is P0 bit for bit
@@ -1973,18 +1975,22 @@ void linear_block_kernel(const LinearArgs a) {
 #pragma unroll
     for (int t = 0; t < TN; ++t) z[mt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // prologue: chunks cbeg .. cbeg + NS - 2 in flight; cbeg and cbeg + 1 landed
-#pragma unroll
-  for (int p = 0; p < NS - 1; ++p) issue_copies(min(cbeg + p, last), stage_of(cbeg + p));
-  __builtin_amdgcn_s_waitcnt(wait_vmcnt(BL::kCopies * (NS - 3)));
-  ring_barrier();
+  // prologue of a chunk range from c0: chunks c0 .. c0 + NS - 2 in flight;
+  // c0 and c0 + 1 landed
   half8 af[8], bc[TN], bn[TN];
   uint32_t wa[TN][ND], wb[TN][ND];
-  read_a(af, stage_of(cbeg));
-  read_w(wa, stage_of(cbeg));
+  auto prologue = [&](int c0) {
 #pragma unroll
-  for (int t = 0; t < TN; ++t) bc[t] = decode8<BITS>(wa[t], bl.shift, cbc);
-  read_w(wa, stage_of(cbeg + 1));
+    for (int p = 0; p < NS - 1; ++p) issue_copies(min(c0 + p, last), stage_of(c0 + p));
+    __builtin_amdgcn_s_waitcnt(wait_vmcnt(BL::kCopies * (NS - 3)));
+    ring_barrier();
+    read_a(af, stage_of(c0));
+    read_w(wa, stage_of(c0));
+#pragma unroll
+    for (int t = 0; t < TN; ++t) bc[t] = decode8<BITS>(wa[t], bl.shift, cbc);
+    read_w(wa, stage_of(c0 + 1));
+  };
+  prologue(cbeg);
 
   // one chunk: MFMAs of chunk cc (A in af, B in bc; FIRST: the chain's first
   // chunk, accumulating onto zero); meanwhile the words of chunk cc + 1 (wa)
@@ -2131,6 +2137,44 @@ void linear_block_kernel(const LinearArgs a) {
   for (int i = 0; i < 2; ++i) {
     const int r16 = 16 * (wave + 4 * i);
     if (row_base + r16 < M) epilogue_rows_lds<4>(zb + r16 * 132, 132, ec, lane, m, col0, row_base + r16, M);
+  }
+
+  if constexpr (CHAINED) {
+    // Left blocks (one row block, more blocks than workgroups): the launch
+    // has a workgroup for each of its first own_blocks blocks only; the S
+    // splits of each of the left_blocks blocks after them go one to a
+    // workgroup, which after its own block runs that split's chain and
+    // stores the partial ([split][left block of the member] x 8 KB per
+    // 16-row tile, at the member's partials); the split-fold launch after
+    // this one adds them in split order and finishes those blocks' rows.
+    const int task = tile;
+    if (a.left_blocks > 0 && task < a.left_blocks * S) {   // uniform
+      const int lb = task / S, sp = task - lb * S;
+      const int gb = a.own_blocks + lb;                      // the left block among the launch's blocks
+      int j2 = 0;
+      if (a.n_members > 1 && gb >= a.m[1].wg_begin) j2 = 1;
+      if (a.n_members > 2 && gb >= a.m[2].wg_begin) j2 = 2;
+      const MemberArgs &m2 = a.m[j2];
+      const int nb2 = gb - m2.wg_begin;
+      const int first_left = max(0, a.own_blocks - m2.wg_begin);   // the member's first left block
+      const int c0 = (int)(((int64_t)sp * C) / S), c1 = (int)(((int64_t)(sp + 1) * C) / S);
+      ra = xr_rsrc(m2);
+      rw = make_rsrc(m2.words + (int64_t)nb2 * m2.block_stride, (uint32_t)m2.block_stride);
+      last = c1 - 1;
+      __syncthreads();                                       // the epilogue's LDS reads are done
+      prologue(c0);
+      chain(c0, c1);
+      const __amdgpu_buffer_rsrc_t rp =
+          make_rsrc(m2.partials + ((int64_t)sp * (m2.n_blocks - first_left) + (nb2 - first_left)) * (8 * 8 * 256),
+                    8 * 8 * 1024);
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+        for (int t = 0; t < TN; ++t)
+          if (16 * mt + 4 * g < M)
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[mt][t]), rp,
+                                                   (mt * 8 + t0 + t) * 1024 + 16 * lane, 0, 0);
+    }
   }
 }
 
