@@ -1375,8 +1375,8 @@ __device__ __forceinline__ void compute_tile_chunk(const char *buf, const uint32
   }
 }
 
-// Exchanged (one split per workgroup, about 150 VGPRs): three workgroups per
-// CU, so that the down projection's 640 workgroups at 65-128 rows run in one
+// Exchanged (one split per workgroup, about 165 VGPRs): three workgroups per
+// CU, so that the down projection's 640 workgroups at 49-128 rows run in one
 // round instead of 1.25 (-5 to -9 %); chained (about 230 VGPRs): two.
 template <int BITS, bool CHAINED>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(CHAINED ? 2 : 3, CHAINED ? 2 : 3)))
@@ -1848,16 +1848,18 @@ void linear_wide_kernel(const LinearArgs a) {
 
 // ------------------------------------------------------------ linear, 128-row block tiles
 //
-// Up to 128 rows (and prompt launches with exchanged splits). A workgroup of
+// Mid rows of wide weights and prompt rows of all but long-split weights
+// (chained; the exchanged form only when forced). A workgroup of
 // 4 waves computes 128 rows x one 128-column block; wave w owns all 128 rows
 // of column tiles 2w, 2w + 1 (8 x 2 MFMA tiles), so each decoded B operand
 // feeds 8 MFMAs, and two workgroups fit on a CU (two waves per SIMD). The
 // operands reach LDS as in the 128 x 256 tiling: buffer-to-LDS copies into a
 // 6-stage ring, input operands stored linearly, tile rows of words in padded
-// slots. Chained: every split of the block, folded in split order. Exchanged:
-// one split per workgroup, its partial stored in the fragment layout; the
-// block's last arriving workgroup adds the S partials in split order, resets
-// the counter and finishes the rows.
+// slots. Chained: every split of the block, folded in split order (then,
+// with left blocks, one split of a left block, its partial stored for the
+// split-fold launch). Exchanged: one split per workgroup, its partial stored
+// in the fragment layout; the block's last arriving workgroup adds the S
+// partials in split order, resets the counter and finishes the rows.
 
 template <int BITS>
 struct BlockLds {
@@ -2047,7 +2049,7 @@ void linear_block_kernel(const LinearArgs a) {
     }
   };
   // z += the split's chain sum. The accumulators are left to the compiler:
-  // in VGPRs (205-213 of the 256 two waves per SIMD allow) the fold is one
+  // in VGPRs (209-221 of the 256 two waves per SIMD allow) the fold is one
   // add per value instead of a read out of AGPRs and an add, about 0.4
   // fewer VALU instructions per MFMA (8192-row layer 5.26-5.29 -> 5.18 ms)
   auto fold = [&]() {
