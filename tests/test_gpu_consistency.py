@@ -317,22 +317,23 @@ def test_two_phase_calls_equal_the_group_call(M, force):
 
 
 def test_spread_launch_over_several_row_blocks():
-    """The {gate, up} pair (272 blocks at S = 15) at 17-48 rows runs the
+    """The {gate, up} pair (272 blocks at S = 15) at 17-32 rows runs the
     spread launch once per 16-row block in one grid (the left blocks'
-    partials and counters per row block), and forced at 64 rows: byte for
-    byte the chained 16-row launch and the exchanged one, counters zero
-    afterwards."""
+    partials and counters per row block), and forced at 40, 48 and 64 rows
+    (where the automatic choice is the 128-row block tiling with its left
+    blocks): byte for byte the automatic launch, the chained 16-row launch
+    and the exchanged one, counters zero afterwards."""
     K = synth.HIDDEN
     ws_ = [G.upload(G.layer("spread-rb", n, K, synth.INTERMEDIATE, 3)) for n in ("gate", "up")]
     xd = G.dev_bf16(G.xbits("spread-rb", 64, K))
     ws = ex().Workspace().reserve(ws_, 64)
     for M in (17, 31, 32, 40, 48, 64):
-        ex().exl3_test_force(*((1, 2, 0) if M == 64 else (-1, -1, 0)))
-        ws.reserve(ws_, M)                                  # forced at 64 rows: that launch's workspace
+        ex().exl3_test_force(*((1, 2, 0) if M > 32 else (-1, -1, 0)))
+        ws.reserve(ws_, M)                                  # forced above 32 rows: that launch's workspace
         auto = [G.host_u16(y) for y in G.run_group(ws_, xd, M=M, ws=ws, tag="spread over row blocks")]
         ex().exl3_test_force(-1, -1, 0)
         assert int(ws.counters().abs().sum()) == 0, M
-        for force in ((1, 1, 0), (1, 0, 0)):
+        for force in ((1, 1, 0), (1, 0, 0), (-1, -1, 0)):
             ex().exl3_test_force(*force)
             ws.reserve(ws_, M)
             other = [G.host_u16(y) for y in G.run_group(ws_, xd, M=M, ws=ws, tag=f"forced {force}")]

@@ -10,9 +10,9 @@ output is its own single-weight launch's, which the oracle defines).
   workgroups' spare waves through the workspace). Every such left block is
   compared with the oracle, beside the first, last and a random block of
   each member.
-* The 3-bit {gate, up} pair of the 3.5 bpw MLP at 17, 32 and 48 rows: the
-  spread launch over several 16-row blocks in one grid; at 49, 100 and 128
-  rows the chained 128-row block tiling with one workgroup per CU, the
+* The 3-bit {gate, up} pair of the 3.5 bpw MLP at 17, 24 and 32 rows: the
+  spread launch over several 16-row blocks in one grid; at 33, 48, 49, 100
+  and 128 rows the chained 128-row block tiling with one workgroup per CU, the
   blocks past one per CU split one chain to a workgroup and finished by the
   split-fold launch (every such block against the oracle, and rows 0 and
   M - 1 byte for byte against one-row calls).
@@ -91,16 +91,16 @@ def test_gate_up_group_spread_launch_vs_oracle(M):
     check_group(("gate", "up"), M, 4, "group-oracle", "x")
 
 
-@pytest.mark.parametrize("M", [17, 32, 48])
+@pytest.mark.parametrize("M", [17, 24, 32])
 def test_gate_up_3bit_spread_over_row_blocks_vs_oracle(M):
     """The 3.5 bpw MLP's {gate, up} pair at mid rows: the spread launch once
     per 16-row block in one grid, left blocks per row block."""
     check_group(("gate", "up"), M, 3, "group-oracle-c3", "x")
 
 
-@pytest.mark.parametrize("M", [49, 100, 128])
+@pytest.mark.parametrize("M", [33, 48, 49, 100, 128])
 def test_gate_up_3bit_block_tiling_left_blocks_vs_oracle(M):
-    """The 3.5 bpw MLP's {gate, up} pair at 49-128 rows: 256 block workgroups,
+    """The 3.5 bpw MLP's {gate, up} pair at 33-128 rows: 256 block workgroups,
     the 16 left blocks' splits one per workgroup after its own block."""
     check_group(("gate", "up"), M, 3, "group-oracle-c3", "x")
     layers = [G.layer("group-oracle-c3", n, K, COLS[n], 3) for n in ("gate", "up")]

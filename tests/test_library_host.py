@@ -254,7 +254,7 @@ def test_workspace_for_max_rows_covers_smaller_calls(lib):
 
 def test_group_workspace_for_max_rows_covers_smaller_calls(lib):
     """The same for groups, at every row count where the automatic choice
-    changes form (the {gate, up} pair takes the spread launch up to 48 rows,
+    changes form (the {gate, up} pair takes the spread launch up to 32 rows,
     over several 16-row blocks above 16, then the 128-row block tiling; the
     {q, k, v} group the 16-row forms, then 128-row tiles)."""
     ex.exl3_test_mock(True)
@@ -341,8 +341,9 @@ def test_rotation_runs_inside_the_linear_launch_up_to_32_rows(lib):
             assert launches(M) == 1, M
         ex.exl3_test_force(-1, -1, 0)
         # the {gate, up} pair: one launch at 16 rows (spread launch, one row
-        # block); at 17-48 rows the spread launch covers several row blocks
-        # and keeps its rotation launch
+        # block); at 17-32 rows the spread launch covers several row blocks
+        # and keeps its rotation launch; at 33 and 48 rows the 128-row block
+        # tiling with its left blocks (rotation, tiling, split fold)
         g = fake_weight(5120, 17408, 4, base=0x60000000)
         u = fake_weight(5120, 17408, 4, base=0x70000000)
         gu = ex._wlist([g, u])
@@ -350,7 +351,7 @@ def test_rotation_runs_inside_the_linear_launch_up_to_32_rows(lib):
         ws2 = ex.exl3_workspace_t(0x20000000, need2, cb2)
         ys2 = (ctypes.c_void_p * 2)(0x80000000, 0x90000000)
         ld2 = (ctypes.c_int64 * 2)(17408, 17408)
-        for M, n in ((16, 1), (17, 2), (48, 2)):
+        for M, n in ((16, 1), (17, 2), (32, 2), (33, 3), (48, 3)):
             assert lib.exl3_linear_group(2, gu, 0x30000000, 5120, M, ys2, ld2, ctypes.byref(ws2), None) == 0
             assert ex.exl3_test_mock_counts()[0] == n, M
         # the two-phase calls never fuse

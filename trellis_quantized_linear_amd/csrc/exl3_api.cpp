@@ -137,6 +137,22 @@ constexpr int64_t kChainedMinBlocks16 = 512;
 // for the 128-row block tiling).
 constexpr int64_t kSpreadMaxRows = 48;
 
+// Weights whose blocks exceed the CUs by a few (the 3-bit {gate, up} pair:
+// 272 blocks on 256 CUs) leave the spread launch above this many rows for the
+// chained 128-row block tiling with its left blocks: at 33, 40 and 48 rows
+// 70-74 us (split-fold launch included) against 73-79 us over three 16-row
+// blocks; the same bits either way.
+constexpr int64_t kSpreadMaxRowsLeft = 32;
+
+// The chained 128-row block tiling can give the blocks past one per CU to
+// the workgroups as single splits: one plan of at most 16 splits for every
+// member, and no more left splits than CUs.
+bool block_left_fits(const MemberPlan *mp, int n, int64_t blocks, int64_t ncu) {
+  for (int j = 1; j < n; ++j)
+    if (mp[j].splits != mp[0].splits) return false;
+  return mp[0].splits <= 16 && blocks > ncu && (blocks - ncu) * mp[0].splits <= ncu;
+}
+
 // Mid-M rows (17..128) with the automatic tiling: the row tiling and
 // whether the splits of a block fold inside one workgroup (chained) or
 // exchange through the workspace, chosen from measurements on MI355X of the
@@ -200,8 +216,12 @@ Launch choose_launch(const MemberPlan *mp, int n, int64_t M) {
   const bool wide = mt == 16 || (mt == -1 && M > 128 && long_chains);
   int mid_chained = -1;
   bool mid_spread = false;
+  const bool left_fits = block_left_fits(mp, n, blocks, ncu);
   if (mt == 16) {
     mt = 8;
+  } else if (mt == -1 && M > kSpreadMaxRowsLeft && M <= 128 && left_fits && !all_single) {
+    mt = 8;
+    mid_chained = 1;
   } else if (mt == -1 && M > 16 && M <= kSpreadMaxRows && sp_own > 0) {
     mt = 1;
     mid_spread = true;
@@ -281,11 +301,8 @@ Launch choose_launch(const MemberPlan *mp, int n, int64_t M) {
   // blocks past one per CU would run as second workgroups on a few CUs and
   // set the launch time; instead each CU's workgroup runs one split of one
   // of them after its own block, and the split-fold launch adds those
-  // partials. Every member with one plan S.
-  bool one_plan = true;
-  for (int j = 1; j < n; ++j) one_plan = one_plan && mp[j].splits == mp[0].splits;
-  if (L.kernel == exl3::kBlock128 && L.chained && L.row_blocks == 1 && one_plan && mp[0].splits <= 16 &&
-      blocks > ncu && (blocks - ncu) * mp[0].splits <= ncu) {
+  // partials.
+  if (L.kernel == exl3::kBlock128 && L.chained && L.row_blocks == 1 && left_fits) {
     L.block_left = true;
     L.own_blocks = ncu;
     L.left_blocks = blocks - ncu;
