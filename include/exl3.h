@@ -271,8 +271,10 @@ int exl3_test_fuse_rotation(int32_t on, int32_t spin_limit);
  *            2 the spread launch (16-row tiles, one S <= 15 for every
  *            member; otherwise as 1): a 16-wave workgroup per (16-row block,
  *            owned block), its spare waves taking splits of the remaining
- *            blocks (the automatic choice at up to 48 rows where the block
- *            counts fit, e.g. the {gate, up} pair),
+ *            blocks (the automatic choice at up to 32 rows where the block
+ *            counts fit, e.g. the {gate, up} pair; up to 48 rows where the
+ *            128-row block tiling cannot give its blocks past one per CU
+ *            to the workgroups as single splits),
  *            3 as 0, with each split on two waves of 4 column tiles (16-row
  *            tiles; the automatic choice when 16-row exchanged launches have
  *            at most one split chain per SIMD).
