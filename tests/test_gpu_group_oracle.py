@@ -16,6 +16,8 @@ output is its own single-weight launch's, which the oracle defines).
   blocks past one per CU split one chain to a workgroup and finished by the
   split-fold launch (every such block against the oracle, and rows 0 and
   M - 1 byte for byte against one-row calls).
+* The same pair at 40 rows at widths 2 and 4-8 (the 128-row block tiling
+  with its left blocks at every width).
 * A stress of the relaxed split-K exchange on that headline launch: 10^4
   group calls at 16 rows, bytes compared every 100 calls, counters zero at
   the end (PR #1475, "What this changes": the last arriver resets its
@@ -111,6 +113,16 @@ def test_gate_up_3bit_block_tiling_left_blocks_vs_oracle(M):
         one = [G.host_u16(y) for y in G.run_group(ws_, xd[r:r + 1], M=1, tag=f"row {r} alone")]
         for j in range(2):
             assert np.array_equal(one[j][0], full[j][r]), (M, r, j)
+
+
+@pytest.mark.parametrize("bits", [2, 4, 5, 6, 7, 8])
+def test_gate_up_block_tiling_left_blocks_every_width_vs_oracle(bits):
+    """The {gate, up} pair at 40 rows at the other widths: the same launch
+    (chained 128-row blocks, the left blocks' splits after each workgroup's
+    own block, the split-fold launch), every left block and sampled blocks
+    against the oracle."""
+    check_group(("gate", "up"), 40, bits, "group-oracle-w", "x")
+    assert ex().exl3_test_last_form() == f"linear_block_kernel<{bits}, true>"
 
 
 def test_gate_up_spread_exchange_stress():
