@@ -117,11 +117,13 @@ def test_prompt_rows_equal_decode_rows():
     assert np.array_equal(win, full[128:144])
 
 
-@pytest.mark.parametrize("M", [1, 7, 16, 200])
+@pytest.mark.parametrize("M", [1, 7, 16, 200, 1027])
 def test_group_equals_each_member_alone(M):
     """PR #1467 exl3-midm: a {q, k, v} or {gate, up} group call gives, per
     member, the bytes of that member's solo call, at 1, 7, 16 and 200 prompt
-    rows (two row blocks, the members' tiles side by side in one launch)."""
+    rows (two row blocks, the members' tiles side by side in one launch) and
+    at 1027 rows, where the group's rotation launch reads each 4-row piece of
+    X once for all members (a ragged last piece of 3 rows)."""
     K = synth.HIDDEN
     x = G.xbits("group", M, K)
     xd = G.dev_bf16(x)

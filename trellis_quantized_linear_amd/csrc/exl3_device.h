@@ -349,8 +349,10 @@ __device__ __forceinline__ void epilogue_rows_lds(float *zrows, int pitch, const
 //
 // Xr = fp16( FWHT128(X ⊙ suh) · 2^-4 ) per 128-chunk of K, the same
 // butterflies as the output transform: levels h = 1, 2, ..., 64 in that order,
-// each pair (i, i + h) -> (a + b, a - b) in fp32. One wave per (member, 4 rows,
-// 128-chunk): lane l (c = l % 16, g = l / 16) holds elements 8c .. 8c+7 of row
+// each pair (i, i + h) -> (a + b, a - b) in fp32. One wave per (4 rows,
+// 128-chunk), reading X once and rotating it for each member in turn (the
+// in-launch rotation: per member and 128-chunk, all M <= 32 rows): lane l
+// (c = l % 16, g = l / 16) holds elements 8c .. 8c+7 of row
 // 4q + g, so levels 1, 2, 4 pair registers and levels 8, 16, 32, 64 pair
 // lanes c ^ 1, c ^ 2, c ^ 4, c ^ 8 of a 16-lane DPP row. Each lane loads and
 // stores 16 contiguous bytes; Xr leaves in the MFMA slot order (within each

@@ -71,6 +71,10 @@ inline int64_t fused_sync_words(int n_members, int64_t K) { return 1 + (int64_t)
 // Largest sync region a fused launch uses (flags of one workgroup's clear pass).
 constexpr int64_t kMaxFusedFlags = 1024;
 
+// Rotation launches of at least this many (4 rows, 128-chunk) items per
+// member read X once for all members (a thousand rows at K = 5120).
+constexpr int64_t kRotSharedItems = 10240;
+
 struct RotArgs {
   const uint16_t *x;          // bf16 [M][ldx]
   const uint16_t *suh[kMaxMembers];
@@ -82,6 +86,8 @@ struct RotArgs {
   int32_t natural_order;      // 1: natural K order (test hook), 0: MFMA slot order
   int32_t chunk_major;        // 1: Xr element (row, k) at ((k / 32) * M + row) * 32 + k % 32
                               // (the layout the spread launch reads), 0: row * K + k
+  int32_t shared_x;           // 1: a wave per (4 rows, 128-chunk) rotates X for every member;
+                              // 0: a wave per (member, 4 rows, 128-chunk)
 };
 
 struct DequantArgs {

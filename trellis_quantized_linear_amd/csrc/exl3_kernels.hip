@@ -1,7 +1,8 @@
 // HIP kernels of the EXL3 trellis-quantized linear for gfx950 (MI355X), other
 // than the linear kernels themselves (exl3_device.h, exl3_linear_bits.hip):
 //
-//   rot_kernel      Xr = fp16(FWHT128(X * suh) * 2^-4) for up to three members
+//   rot_kernel      Xr = fp16(FWHT128(X * suh) * 2^-4) for up to three members,
+//                   X read once
 //   dequant_kernel  test hook: the decoded weights, through the same decoder
 //   codebook_kernel test hook: the codebook on arbitrary states
 //   fill_zero       zeroes a grown counter region on the caller's stream
@@ -35,19 +36,25 @@ __global__ __launch_bounds__(kThreads) void rot_kernel(const RotArgs a) {
   const int kc = a.K >> 7;
   const int quads = (a.M + 3) >> 2;
   const int64_t per_member = (int64_t)quads * kc;
-  if (item >= per_member * a.n_members) return;
-  const int j = (int)(item / per_member);
-  const int64_t rem = item - (int64_t)j * per_member;
+  // shared_x: item = (quad, chunk) and every member; else item = (member,
+  // quad, chunk)
+  const int n_items = a.shared_x ? 1 : a.n_members;
+  if (item >= per_member * n_items) return;
+  const int j0 = a.shared_x ? 0 : (int)(item / per_member);
+  const int j1 = a.shared_x ? a.n_members : j0 + 1;
+  const int64_t rem = item - (int64_t)j0 * per_member;
   const int quad = (int)(rem / kc);
   const int chunk = (int)(rem - (int64_t)quad * kc);
   const int row = 4 * quad + g;
   if (row >= a.M) return;                                // no cross-lane step below mixes rows
-  const uint16_t *suh = j == 0 ? a.suh[0] : (j == 1 ? a.suh[1] : a.suh[2]);
-  uint16_t *xr = j == 0 ? a.xr[0] : (j == 1 ? a.xr[1] : a.xr[2]);
   const int k0 = chunk * 128 + 8 * c;
-  const u32x4 out = rot_lane(load8_u16(a.x + (int64_t)row * a.ldx + k0), load8_u16(suh + k0), c, a.natural_order != 0);
   const int64_t at = a.chunk_major ? ((int64_t)(k0 >> 5) * a.M + row) * 32 + (k0 & 31) : (int64_t)row * a.K + k0;
-  *(u32x4 *)(xr + at) = out;
+  const u32x4 xw = load8_u16(a.x + (int64_t)row * a.ldx + k0);
+  for (int j = j0; j < j1; ++j) {                        // uniform; each member as if alone
+    const uint16_t *suh = j == 0 ? a.suh[0] : (j == 1 ? a.suh[1] : a.suh[2]);
+    uint16_t *xr = j == 0 ? a.xr[0] : (j == 1 ? a.xr[1] : a.xr[2]);
+    *(u32x4 *)(xr + at) = rot_lane(xw, load8_u16(suh + k0), c, a.natural_order != 0);
+  }
 }
 
 // ------------------------------------------------------------ split fold
@@ -185,8 +192,16 @@ void form_name(char *buf, size_t n, int bits, int kernel, bool chained, int rows
   linear_form_name(buf, n, bits, kernel, chained, rows);
 }
 
-int launch_rot(const RotArgs &a, void *stream) {
-  const int64_t items = (int64_t)a.n_members * ((a.M + 3) / 4) * (a.K / 128);
+int launch_rot(const RotArgs &a_in, void *stream) {
+  // Prompt rows: X read once for all members (a layer's {q, k, v} at 8192
+  // rows 504 -> 336 MB, the 8192-row layer 5.33-5.34 -> 5.29 ms). A few
+  // rows: a wave per member, whose rotation launch waits on one X load per
+  // wave either way (the decode step 45.1-45.9 us with it, 46.4-46.9 us
+  // with X shared).
+  RotArgs a = a_in;
+  const int64_t per_member = (int64_t)((a.M + 3) / 4) * (a.K / 128);
+  a.shared_x = a.n_members > 1 && per_member >= kRotSharedItems ? 1 : 0;
+  const int64_t items = per_member * (a.shared_x ? 1 : a.n_members);
   const int64_t wgs = (items + kWaves - 1) / kWaves;
   (void)hipGetLastError();
   hipLaunchKernelGGL(rot_kernel, dim3((unsigned)wgs), dim3(kThreads), 0, (hipStream_t)stream, a);
