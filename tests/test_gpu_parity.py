@@ -106,11 +106,12 @@ def test_dequant_fills_from_the_pages(bits):
 
 # ------------------------------------------------------------ rotation
 
-@pytest.mark.parametrize("K,M", [(256, 3), (5120, 16), (17408, 5)])
+@pytest.mark.parametrize("K,M", [(256, 3), (5120, 16), (17408, 5), (5120, 1101)])
 def test_rot_in_vs_oracle(K, M):
     """fp32 butterflies then one fp16 rounding, against float64 then one fp16
     rounding: equal except where the fp32 sum lands across an fp16 rounding
-    boundary, and then by one fp16 ulp."""
+    boundary, and then by one fp16 ulp (1101 rows: a ragged last 4-row
+    piece)."""
     torch = G.torch_mod()
     L = G.layer("rot", "w", K, 128, 4)
     x = G.xbits("rot", M, K)
