@@ -9,6 +9,7 @@ allocates nothing and zeroes nothing).
 """
 
 import ctypes
+import os
 import re
 
 import pytest
@@ -463,3 +464,15 @@ def test_split_fold_launch_after_the_exchanged_128_row_tiling(lib):
     need17, cb17 = ex.exl3_workspace_need([w], 128)
     ws = ex.exl3_workspace_t(0x200000000, need17, cb17)
     assert call(128) == (2, "linear_tile_kernel<4, false>")
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU: asked for two it exits with status 2 and a
+    message naming the request, before it touches a device."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120, cwd=root)
+    assert r.returncode == 2, (r.returncode, r.stdout, r.stderr)
+    assert "one GPU" in r.stdout + r.stderr and "2" in r.stdout + r.stderr
