@@ -297,7 +297,7 @@ Launch choose_launch(const MemberPlan *mp, int n, int64_t M) {
   for (int j = 0; j < n; ++j) max_splits = std::max(max_splits, mp[j].splits);
   L.fold_launch = L.kernel == exl3::kTile128 && !L.chained && max_splits <= 16;
   // The chained 128-row block tiling over one row block with a few more
-  // blocks than CUs ({gate, up} at 49-128 rows: 272 blocks on 256 CUs): the
+  // blocks than CUs ({gate, up} at 33-128 rows: 272 blocks on 256 CUs): the
   // blocks past one per CU would run as second workgroups on a few CUs and
   // set the launch time; instead each CU's workgroup runs one split of one
   // of them after its own block, and the split-fold launch adds those
