@@ -43,8 +43,10 @@ FORMS = {
     "linear_spread_kernel<{b}> +rot": (4, [(256, [34816], 7, "rot")]),
     "linear_spread_rows_kernel<{b}>": (4, [(256, [34816], 17, ""), (256, [17408, 17408], 32, "")]),
     # 128-row tilings
-    "linear_block_kernel<{b}, true>": (2, [(256, [34816], 49, ""), (256, [17408, 17408], 33, ""), (128, [128], 129, ""),
+    "linear_block_kernel<{b}, true>": (2, [(256, [34816], 65, ""), (256, [17408, 17408], 100, ""), (128, [128], 129, ""),
                                           (256, [384], 300, ""), (256, [1024, 256, 256], 200, "")]),
+    # 64-row block tiling: a few more blocks than CUs at 33-64 rows (left blocks as single splits)
+    "linear_block64_kernel<{b}>": (2, [(256, [34816], 33, ""), (256, [17408, 17408], 64, "")]),
     "linear_tile_kernel<{b}, false>": (3, [(16384, [128], 97, ""), (16384, [128, 256], 64, "")]),
     # prompt rows of long-split weights (down): 128 rows x 2 blocks (the last pair of an odd count: 1)
     "linear_wide_kernel<{b}>": (1, [(16384, [128], 129, ""), (16384, [384], 300, ""), (17408, [256, 128], 200, "")]),

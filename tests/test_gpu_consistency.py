@@ -343,6 +343,25 @@ def test_spread_launch_over_several_row_blocks():
             assert all(np.array_equal(a, b) for a, b in zip(auto, other)), (M, force)
 
 
+def test_64_row_block_tiling_equals_the_128_row_one():
+    """The {gate, up} pair (272 blocks) at 33, 48 and 64 rows runs 64-row
+    block workgroups with left blocks; forced to 128-row workgroups (the same
+    left blocks and split-fold launch) it gives the same bytes."""
+    K = synth.HIDDEN
+    ws_ = [G.upload(G.layer("block64", n, K, synth.INTERMEDIATE, 3)) for n in ("gate", "up")]
+    xd = G.dev_bf16(G.xbits("block64", 64, K))
+    for M in (33, 48, 64):
+        auto = [G.host_u16(y) for y in G.run_group(ws_, xd, M=M, tag="64-row workgroups")]
+        assert ex().exl3_test_last_form() == "linear_block64_kernel<3>", M
+        ex().exl3_test_force(8, 1, 0)
+        try:
+            forced = [G.host_u16(y) for y in G.run_group(ws_, xd, M=M, tag="128-row workgroups")]
+            assert ex().exl3_test_last_form() == "linear_block_kernel<3, true>", M
+        finally:
+            ex().exl3_test_force(-1, -1, 0)
+        assert all(np.array_equal(a, b) for a, b in zip(auto, forced)), M
+
+
 def test_split_fold_launch_equals_the_chained_fold():
     """Down-shaped weight (K 17408: long splits) at 100 and 128 rows: the
     exchanged 2 x 2 tiling whose partials the split-fold launch adds gives

@@ -12,11 +12,12 @@ output is its own single-weight launch's, which the oracle defines).
   each member.
 * The 3-bit {gate, up} pair of the 3.5 bpw MLP at 17, 24 and 32 rows: the
   spread launch over several 16-row blocks in one grid; at 33, 48, 49, 100
-  and 128 rows the chained 128-row block tiling with one workgroup per CU, the
+  and 128 rows the chained block tiling (64-row workgroups up to 64 rows,
+  128-row ones above) with one workgroup per CU, the
   blocks past one per CU split one chain to a workgroup and finished by the
   split-fold launch (every such block against the oracle, and rows 0 and
   M - 1 byte for byte against one-row calls).
-* The same pair at 40 rows at widths 2 and 4-8 (the 128-row block tiling
+* The same pair at 40 rows at widths 2 and 4-8 (the 64-row block tiling
   with its left blocks at every width).
 * A stress of the relaxed split-K exchange on that headline launch: 10^4
   group calls at 16 rows, bytes compared every 100 calls, counters zero at
@@ -100,9 +101,10 @@ def test_gate_up_3bit_spread_over_row_blocks_vs_oracle(M):
     check_group(("gate", "up"), M, 3, "group-oracle-c3", "x")
 
 
-@pytest.mark.parametrize("M", [33, 48, 49, 100, 128])
+@pytest.mark.parametrize("M", [33, 48, 49, 64, 65, 100, 128])
 def test_gate_up_3bit_block_tiling_left_blocks_vs_oracle(M):
-    """The 3.5 bpw MLP's {gate, up} pair at 33-128 rows: 256 block workgroups,
+    """The 3.5 bpw MLP's {gate, up} pair at 33-128 rows (64-row workgroups up
+    to 64 rows, 128-row ones above): 256 block workgroups,
     the 16 left blocks' splits one per workgroup after its own block."""
     check_group(("gate", "up"), M, 3, "group-oracle-c3", "x")
     layers = [G.layer("group-oracle-c3", n, K, COLS[n], 3) for n in ("gate", "up")]
@@ -118,11 +120,11 @@ def test_gate_up_3bit_block_tiling_left_blocks_vs_oracle(M):
 @pytest.mark.parametrize("bits", [2, 4, 5, 6, 7, 8])
 def test_gate_up_block_tiling_left_blocks_every_width_vs_oracle(bits):
     """The {gate, up} pair at 40 rows at the other widths: the same launch
-    (chained 128-row blocks, the left blocks' splits after each workgroup's
+    (chained 64-row blocks, the left blocks' splits after each workgroup's
     own block, the split-fold launch), every left block and sampled blocks
     against the oracle."""
     check_group(("gate", "up"), 40, bits, "group-oracle-w", "x")
-    assert ex().exl3_test_last_form() == f"linear_block_kernel<{bits}, true>"
+    assert ex().exl3_test_last_form() == f"linear_block64_kernel<{bits}>"
 
 
 def test_gate_up_spread_exchange_stress():

@@ -139,9 +139,10 @@ constexpr int64_t kSpreadMaxRows = 48;
 
 // Weights whose blocks exceed the CUs by a few (the 3-bit {gate, up} pair:
 // 272 blocks on 256 CUs) leave the spread launch above this many rows for the
-// chained 128-row block tiling with its left blocks: at 33, 40 and 48 rows
-// 70-74 us (split-fold launch included) against 73-79 us over three 16-row
-// blocks; the same bits either way.
+// chained block tiling with its left blocks (at 33, 40 and 48 rows 70-74 us
+// on 128-row workgroups, split-fold launch included, against 73-79 us over
+// three 16-row blocks), in 64-row workgroups up to 64 rows: half the MFMAs
+// (the MLP at 33-64 rows 112-129 -> 98-116 us); the same bits every way.
 constexpr int64_t kSpreadMaxRowsLeft = 32;
 
 // The chained 128-row block tiling can give the blocks past one per CU to
@@ -216,11 +217,13 @@ Launch choose_launch(const MemberPlan *mp, int n, int64_t M) {
   const bool wide = mt == 16 || (mt == -1 && M > 128 && long_chains);
   int mid_chained = -1;
   bool mid_spread = false;
+  bool block64 = false;
   const bool left_fits = block_left_fits(mp, n, blocks, ncu);
   if (mt == 16) {
     mt = 8;
   } else if (mt == -1 && M > kSpreadMaxRowsLeft && M <= 128 && left_fits && !all_single) {
-    mt = 8;
+    block64 = M <= 64;
+    mt = block64 ? 4 : 8;
     mid_chained = 1;
   } else if (mt == -1 && M > 16 && M <= kSpreadMaxRows && sp_own > 0) {
     mt = 1;
@@ -283,6 +286,7 @@ Launch choose_launch(const MemberPlan *mp, int n, int64_t M) {
            : spread    ? exl3::kSpread16
            : mt == 1 ? (L.chained ? exl3::kChain16x8 : halves ? exl3::kChain16H : exl3::kChain16)
            : mt == 2 ? exl3::kChain32
+           : block64 ? exl3::kBlock64
            : mt == 4 ? exl3::kNtile64
            : wide && L.chained ? exl3::kWide128
            : !L.chained && long_chains ? exl3::kTile128
@@ -302,7 +306,7 @@ Launch choose_launch(const MemberPlan *mp, int n, int64_t M) {
   // set the launch time; instead each CU's workgroup runs one split of one
   // of them after its own block, and the split-fold launch adds those
   // partials.
-  if (L.kernel == exl3::kBlock128 && L.chained && L.row_blocks == 1 && left_fits) {
+  if ((L.kernel == exl3::kBlock128 || L.kernel == exl3::kBlock64) && L.chained && L.row_blocks == 1 && left_fits) {
     L.block_left = true;
     L.own_blocks = ncu;
     L.left_blocks = blocks - ncu;
@@ -567,7 +571,7 @@ int run_group(int32_t n_members, const exl3_weight_t *const *w, const void *x, i
   // Chunk offsets are 32-bit: chunk-major needs 2 K M < 2^31, which every
   // accepted call meets (check_group).
   const bool tile_cm = (L.kernel == exl3::kTile128 || L.kernel == exl3::kBlock128 || L.kernel == exl3::kWide128 ||
-                        L.kernel == exl3::kQuad128) &&
+                        L.kernel == exl3::kQuad128 || L.kernel == exl3::kBlock64) &&
                        2 * K * M < (int64_t(1) << 31);
   ra.chunk_major = L.kernel == exl3::kSpread16 || tile_cm ? 1 : 0;
   la.xr_chunk_major = tile_cm ? 1 : 0;

@@ -1854,33 +1854,38 @@ void linear_wide_kernel(const LinearArgs a) {
 // (chained; the exchanged form only when forced). A workgroup of
 // 4 waves computes 128 rows x one 128-column block; wave w owns all 128 rows
 // of column tiles 2w, 2w + 1 (8 x 2 MFMA tiles), so each decoded B operand
-// feeds 8 MFMAs, and two workgroups fit on a CU (two waves per SIMD). The
-// operands reach LDS as in the 128 x 256 tiling: buffer-to-LDS copies into a
-// 6-stage ring, input operands stored linearly, tile rows of words in padded
-// slots. Chained: every split of the block, folded in split order (then,
+// feeds 8 MFMAs, and two workgroups fit on a CU (two waves per SIMD).
+// linear_block64_kernel is the same with 64 rows (4 x 2 MFMA tiles a wave)
+// for launches of at most 64 rows. The operands reach LDS as in the
+// 128 x 256 tiling: buffer-to-LDS copies into a 6-stage ring, input operands
+// stored linearly, tile rows of words in padded slots. Chained: every split of the block, folded in split order (then,
 // with left blocks, one split of a left block, its partial stored for the
 // split-fold launch). Exchanged: one split per workgroup, its partial stored
 // in the fragment layout; the block's last arriving workgroup adds the S
 // partials in split order, resets the counter and finishes the rows.
 
-template <int BITS>
+template <int BITS, int RT = 8>
 struct BlockLds {
-  static constexpr int kA = 128 * 64;                        // input tile of one chunk
+  static constexpr int kA = RT * 16 * 64;                    // input tile of one chunk (RT * 16 rows)
   static constexpr int kRowBytes = 256 * BITS;               // one tile row (8 tiles) of the block
   static constexpr int kRow = 2048 + 128;                    // its slot: two 1 KB halves (4 tiles each) + 128 bytes
   static constexpr int kStage = kA + 2 * kRow;
   static constexpr int kStages = 6;
   static constexpr int kRing = kStages * kStage;
-  static constexpr int kZ = 128 * 132 * 4;                   // epilogue: the block's Z, 132-float rows
+  static constexpr int kZ = RT * 16 * 132 * 4;               // epilogue: the block's Z, 132-float rows
   static constexpr int kBytes = kRing > kZ ? kRing : kZ;
   static constexpr int kPiece = kRowBytes / 2;               // bytes of a half tile row (4 tiles, <= 1 KB)
-  static constexpr int kCopies = 3;                          // copies per wave and chunk: 2 input operands + a piece
+  static constexpr int kCopies = RT / 4 + 1;                 // copies per wave and chunk: RT / 4 input operands + a piece
 };
 
-template <int BITS, bool CHAINED>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void linear_block_kernel(const LinearArgs a) {
-  using BL = BlockLds<BITS>;
+// RT row tiles of 16 per workgroup: 8 (128 rows) or, chained, 4 (64 rows,
+// for launches of at most 64 rows: half the MFMAs, the same bits per row).
+template <int BITS, bool CHAINED, int RT>
+__device__ __forceinline__ void block_body(const LinearArgs &a) {
+  static_assert(RT == 8 || (RT == 4 && CHAINED), "64-row workgroups: chained only");
+  using BL = BlockLds<BITS, RT>;
+  constexpr int R = 16 * RT;                                 // rows per workgroup
+  constexpr int AE = RT / 4;                                 // input operands each wave copies per chunk
   using TR = BitsTraits<BITS>;
   constexpr int NS = BL::kStages;
   constexpr int ND = TR::kDwords;
@@ -1911,26 +1916,26 @@ void linear_block_kernel(const LinearArgs a) {
   const int sg = r2 - (r2 / groups) * groups;
   const int M = a.M, K = a.K, C = a.chunks;
   const int S = m.splits;
-  const int row_base = rb * 128;
+  const int row_base = rb * R;
   const int col0 = nb * kBlockCols;
 
   __shared__ __attribute__((aligned(16))) char lds[BL::kBytes];
 
-  // copies: wave w moves input operands 2w + e (lane l brings row
-  // 16 (2w + e) + l % 16, 16-byte column l / 16) and half w % 2 of tile row
-  // w / 2 of every chunk
+  // copies: wave w moves input operands AE w + e (lane l brings row
+  // 16 (AE w + e) + l % 16, 16-byte column l / 16) and half w % 2 of tile
+  // row w / 2 of every chunk
   auto xr_rsrc = [&](const MemberArgs &mm) {
     return a.xr_chunk_major ? make_rsrc(mm.xr + (int64_t)row_base * kChunk, (uint32_t)(C * M - row_base) * 64u)
-                            : make_rsrc(mm.xr + (int64_t)row_base * K, (uint32_t)min(M - row_base, 128) * (uint32_t)K * 2u);
+                            : make_rsrc(mm.xr + (int64_t)row_base * K, (uint32_t)min(M - row_base, R) * (uint32_t)K * 2u);
   };
   __amdgpu_buffer_rsrc_t ra = xr_rsrc(m);
   // Xr chunk-major (each chunk's M rows contiguous, 64 bytes a row) or row-major
   const int a_row = a.xr_chunk_major ? 64 : 2 * K;           // bytes from one row to the next
   const int a_step = a.xr_chunk_major ? 64 * M : 64;         // bytes from one chunk to the next
-  uint32_t va[2];
+  uint32_t va[AE];
 #pragma unroll
-  for (int e = 0; e < 2; ++e) {
-    const int r = 16 * (2 * wave + e) + c;
+  for (int e = 0; e < AE; ++e) {
+    const int r = 16 * (AE * wave + e) + c;
     va[e] = row_base + r < M ? (uint32_t)(r * a_row + 16 * g) : kOutOfRange;
   }
   __amdgpu_buffer_rsrc_t rw = make_rsrc(m.words + (int64_t)nb * m.block_stride, (uint32_t)m.block_stride);
@@ -1940,7 +1945,7 @@ void linear_block_kernel(const LinearArgs a) {
   auto stage_of = [&](int i) { return lds + (int)((unsigned)i % NS) * BL::kStage; };
   auto issue_copies = [&](int chunk, char *stage) {
 #pragma unroll
-    for (int e = 0; e < 2; ++e) copy_to_lds(ra, stage + 1024 * (2 * wave + e), va[e], chunk * a_step);
+    for (int e = 0; e < AE; ++e) copy_to_lds(ra, stage + 1024 * (AE * wave + e), va[e], chunk * a_step);
     copy_to_lds(rw, stage + BL::kA + hrow * BL::kRow + half * 1024, vw, chunk * 512 * BITS);
   };
 
@@ -1955,9 +1960,9 @@ void linear_block_kernel(const LinearArgs a) {
     w_rd[d] = (uint32_t)(BL::kA + (g >> 1) * BL::kRow + (t0 >> 2) * 1024 + (t0 & 3) * 32 * BITS) + bl.voff[d] -
               (uint32_t)((g >> 1) * BL::kRowBytes);
   const CbConst cbc = cb_const();
-  auto read_a = [&](half8 (&af)[8], const char *st) {
+  auto read_a = [&](half8 (&af)[RT], const char *st) {
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt) af[mt] = __builtin_bit_cast(half8, *(const u32x4 *)(st + a_rd + 1024 * mt));
+    for (int mt = 0; mt < RT; ++mt) af[mt] = __builtin_bit_cast(half8, *(const u32x4 *)(st + a_rd + 1024 * mt));
   };
   auto read_w = [&](uint32_t (&w)[TN][ND], const char *st) {
 #pragma unroll
@@ -1973,15 +1978,15 @@ void linear_block_kernel(const LinearArgs a) {
 
   // z = P0 + P1 + ... in split order, starting from +0: an MFMA chain that
   // starts from +0 never ends in -0, so +0 + P0 is P0 bit for bit
-  f32x4 acc[8][TN], z[8][TN];
+  f32x4 acc[RT][TN], z[RT][TN];
 #pragma unroll
-  for (int mt = 0; mt < 8; ++mt)
+  for (int mt = 0; mt < RT; ++mt)
 #pragma unroll
     for (int t = 0; t < TN; ++t) z[mt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // prologue of a chunk range from c0: chunks c0 .. c0 + NS - 2 in flight;
   // c0 and c0 + 1 landed
-  half8 af[8], bc[TN], bn[TN];
+  half8 af[RT], bc[TN], bn[TN];
   uint32_t wa[TN][ND], wb[TN][ND];
   auto prologue = [&](int c0) {
 #pragma unroll
@@ -2007,14 +2012,15 @@ void linear_block_kernel(const LinearArgs a) {
     issue_copies(min(cc + NS - 1, last), stage_of(cc + NS - 1));
     read_w(wb, stage_of(cc + 2));
     const char *nxt = stage_of(cc + 1);
+    constexpr int DQ = RT / TN;                              // row tiles per decoded B operand
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt) {
+    for (int mt = 0; mt < RT; ++mt) {
 #pragma unroll
       for (int t = 0; t < TN; ++t)
         acc[mt][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[mt], bc[t], decltype(first)::value ? f32x4{0.f, 0.f, 0.f, 0.f}
                                                                                                : acc[mt][t], 0, 0, 0);
       af[mt] = __builtin_bit_cast(half8, *(const u32x4 *)(nxt + a_rd + 1024 * mt));
-      if ((mt & 3) == 3) bn[mt >> 2] = decode8<BITS>(wa[mt >> 2], bl.shift, cbc);
+      if ((mt + 1) % DQ == 0) bn[mt / DQ] = decode8<BITS>(wa[mt / DQ], bl.shift, cbc);
     }
     if constexpr (CHAINED) {
       // issue order: the copies, the word reads, then per row tile its two
@@ -2023,7 +2029,7 @@ void linear_block_kernel(const LinearArgs a) {
       __builtin_amdgcn_sched_group_barrier(0x020, 3, 0);     // buffer-to-LDS copies
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);     // LDS reads
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 0; i < RT; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // MFMA
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // VALU
@@ -2056,7 +2062,7 @@ void linear_block_kernel(const LinearArgs a) {
   // fewer VALU instructions per MFMA (8192-row layer 5.26-5.29 -> 5.18 ms)
   auto fold = [&]() {
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt)
+    for (int mt = 0; mt < RT; ++mt)
 #pragma unroll
       for (int t = 0; t < TN; ++t)
 #pragma unroll
@@ -2077,7 +2083,7 @@ void linear_block_kernel(const LinearArgs a) {
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     const __amdgpu_buffer_rsrc_t rp = make_rsrc(partial_frag(m, sg, rb, nb, RB, 8), 8 * 8 * 1024);
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt)
+    for (int mt = 0; mt < RT; ++mt)
 #pragma unroll
       for (int t = 0; t < TN; ++t)
         if (row_base + 16 * mt + 4 * g < M) {
@@ -2106,12 +2112,12 @@ void linear_block_kernel(const LinearArgs a) {
     // stale bytes (in bounds: whole 128-row blocks) that no row of the
     // epilogue uses.
     for (int s0 = 0; s0 < S; s0 += 2) {
-      u32x4 v[2][8][TN];
+      u32x4 v[2][RT][TN];
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const __amdgpu_buffer_rsrc_t rq = make_rsrc(partial_frag(m, min(s0 + u, S - 1), rb, nb, RB, 8), 8 * 8 * 1024);
 #pragma unroll
-        for (int mt = 0; mt < 8; ++mt)
+        for (int mt = 0; mt < RT; ++mt)
 #pragma unroll
           for (int t = 0; t < TN; ++t)
             v[u][mt][t] = __builtin_bit_cast(
@@ -2121,16 +2127,16 @@ void linear_block_kernel(const LinearArgs a) {
       for (int u = 0; u < 2; ++u)
         if (s0 + u < S)                                     // uniform
 #pragma unroll
-          for (int mt = 0; mt < 8; ++mt)
+          for (int mt = 0; mt < RT; ++mt)
 #pragma unroll
             for (int t = 0; t < TN; ++t) z[mt][t] = z[mt][t] + __builtin_bit_cast(f32x4, v[u][mt][t]);
     }
   }
 
   // epilogue: the block's Z through LDS
-  float *zb = (float *)lds;                                  // [128][132]
+  float *zb = (float *)lds;                                  // [R][132]
 #pragma unroll
-  for (int mt = 0; mt < 8; ++mt)
+  for (int mt = 0; mt < RT; ++mt)
 #pragma unroll
     for (int t = 0; t < TN; ++t)
 #pragma unroll
@@ -2138,7 +2144,7 @@ void linear_block_kernel(const LinearArgs a) {
   const EpiCols ec = epi_cols(m, col0, lane);
   __syncthreads();
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < RT / 4; ++i) {
     const int r16 = 16 * (wave + 4 * i);
     if (row_base + r16 < M) epilogue_rows_lds<4>(zb + r16 * 132, 132, ec, lane, m, col0, row_base + r16, M);
   }
@@ -2172,7 +2178,7 @@ void linear_block_kernel(const LinearArgs a) {
           make_rsrc(m2.partials + ((int64_t)sp * (m2.n_blocks - first_left) + (nb2 - first_left)) * (8 * 8 * 256),
                     8 * 8 * 1024);
 #pragma unroll
-      for (int mt = 0; mt < 8; ++mt)
+      for (int mt = 0; mt < RT; ++mt)
 #pragma unroll
         for (int t = 0; t < TN; ++t)
           if (16 * mt + 4 * g < M)
@@ -2180,6 +2186,18 @@ void linear_block_kernel(const LinearArgs a) {
                                                    (mt * 8 + t0 + t) * 1024 + 16 * lane, 0, 0);
     }
   }
+}
+
+template <int BITS, bool CHAINED>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void linear_block_kernel(const LinearArgs a) {
+  block_body<BITS, CHAINED, 8>(a);
+}
+
+template <int BITS>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void linear_block64_kernel(const LinearArgs a) {
+  block_body<BITS, true, 4>(a);
 }
 
 // ------------------------------------------------------------ linear, opt-in single-chain prompt tiles
@@ -2390,6 +2408,7 @@ LinearFn pick_linear(int kernel, bool chained, int rows) {
     return rows > 1 ? linear_chain_kernel<BITS, 1, false, 8, 4, kStreamAgain> : linear_chain_kernel<BITS, 1, false, 8, 4>;
   if (kernel == kWide128) return linear_wide_kernel<BITS>;
   if (kernel == kBlock128) return chained ? linear_block_kernel<BITS, true> : linear_block_kernel<BITS, false>;
+  if (kernel == kBlock64) return linear_block64_kernel<BITS>;
   if (kernel == kQuad128) return linear_quad_kernel<BITS>;
   return chained ? pick_kernel<BITS, true>(kernel, rows) : pick_kernel<BITS, false>(kernel, rows);
 }
@@ -2409,6 +2428,7 @@ inline void linear_form_name(char *buf, size_t n, int bits, int kernel, bool cha
     case kChain16H: snprintf(buf, n, "linear_chain_kernel<%d, 1, false, 8, 4, %d>", bits, pol); return;
     case kWide128: snprintf(buf, n, "linear_wide_kernel<%d>", bits); return;
     case kBlock128: snprintf(buf, n, "linear_block_kernel<%d, %s>", bits, ch); return;
+    case kBlock64: snprintf(buf, n, "linear_block64_kernel<%d>", bits); return;
     case kQuad128: snprintf(buf, n, "linear_quad_kernel<%d>", bits); return;
     case kChain16: snprintf(buf, n, "linear_chain_kernel<%d, 1, %s, 4, 8, %d>", bits, ch, pol); return;
     case kChain32: snprintf(buf, n, "linear_chain_kernel<%d, 2, %s, 4, 8, %d>", bits, ch, pol); return;

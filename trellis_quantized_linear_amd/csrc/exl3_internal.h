@@ -110,6 +110,7 @@ enum LinearKernel {
   kBlock128 = 7,    // 128 rows x 1 block per workgroup, 4 waves of 128 x 32
   kQuad128 = 8,     // opt-in single-chain prompt tiles: 128 rows x 4 blocks, 4 waves of 128 x 128
   kChain16H = 9,    // 16 rows, 8 waves, exchanged: two waves per split, 4 column tiles each
+  kBlock64 = 10,    // 64 rows x 1 block per workgroup, 4 waves of 64 x 32 (chained, one row block)
 };
 
 inline int waves_per_wg(int kernel) {
