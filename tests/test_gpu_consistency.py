@@ -343,23 +343,37 @@ def test_spread_launch_over_several_row_blocks():
             assert all(np.array_equal(a, b) for a, b in zip(auto, other)), (M, force)
 
 
-def test_64_row_block_tiling_equals_the_128_row_one():
-    """The {gate, up} pair (272 blocks) at 33, 48 and 64 rows runs 64-row
-    block workgroups with left blocks; forced to 128-row workgroups (the same
-    left blocks and split-fold launch) it gives the same bytes."""
-    K = synth.HIDDEN
-    ws_ = [G.upload(G.layer("block64", n, K, synth.INTERMEDIATE, 3)) for n in ("gate", "up")]
-    xd = G.dev_bf16(G.xbits("block64", 64, K))
-    for M in (33, 48, 64):
-        auto = [G.host_u16(y) for y in G.run_group(ws_, xd, M=M, tag="64-row workgroups")]
-        assert ex().exl3_test_last_form() == "linear_block64_kernel<3>", M
+@pytest.mark.parametrize("what,K,Ns,bits,rows", [
+    ("{gate, up} pair with left blocks", synth.HIDDEN, (synth.INTERMEDIATE, synth.INTERMEDIATE), 3, (33, 48, 64)),
+    ("a 300-block weight, no left blocks", 1024, (300 * 128,), 6, (49, 64))])
+def test_64_row_block_tiling_equals_the_128_row_one(what, K, Ns, bits, rows):
+    """Chained block tilings of at most 64 rows run 64-row workgroups:
+    with left blocks (the {gate, up} pair, 272 blocks at 33-64 rows) and
+    without (300 blocks of 8 splits at 49 and 64 rows, two workgroups on
+    some CUs). Forced to 128-row workgroups (the same left blocks and
+    split-fold launch) they give the same bytes; sampled blocks (first, last,
+    random, and the blocks past one per CU) against the oracle."""
+    layers = [G.layer("block64", f"m{j}", K, N, bits) for j, N in enumerate(Ns)]
+    ws_ = [G.upload(L) for L in layers]
+    x = G.xbits("block64", max(rows), K)
+    xd = G.dev_bf16(x)
+    for M in rows:
+        ys = G.run_group(ws_, xd, M=M, tag=f"{what}, 64-row workgroups")
+        assert ex().exl3_test_last_form() == f"linear_block64_kernel<{bits}>", M
+        auto = [G.host_u16(y) for y in ys]
         ex().exl3_test_force(8, 1, 0)
         try:
-            forced = [G.host_u16(y) for y in G.run_group(ws_, xd, M=M, tag="128-row workgroups")]
-            assert ex().exl3_test_last_form() == "linear_block_kernel<3, true>", M
+            forced = [G.host_u16(y) for y in G.run_group(ws_, xd, M=M, tag=f"{what}, 128-row workgroups")]
+            assert ex().exl3_test_last_form() == f"linear_block_kernel<{bits}, true>", M
         finally:
             ex().exl3_test_force(-1, -1, 0)
         assert all(np.array_equal(a, b) for a, b in zip(auto, forced)), M
+        first = 0
+        for j, (L, y) in enumerate(zip(layers, ys)):
+            nb = L.N // 128
+            blocks = sorted(set(G.sample_blocks(nb, k=3, seed=M + j)) | {b for b in range(nb) if first + b >= 256})
+            first += nb
+            G.assert_close(G.gpu_blocks(y, blocks), G.oracle_blocks(L, x[:M], blocks), what=f"{what} M={M} member {j}")
 
 
 def test_split_fold_launch_equals_the_chained_fold():

@@ -141,8 +141,8 @@ constexpr int64_t kSpreadMaxRows = 48;
 // 272 blocks on 256 CUs) leave the spread launch above this many rows for the
 // chained block tiling with its left blocks (at 33, 40 and 48 rows 70-74 us
 // on 128-row workgroups, split-fold launch included, against 73-79 us over
-// three 16-row blocks), in 64-row workgroups up to 64 rows: half the MFMAs
-// (the MLP at 33-64 rows 112-129 -> 98-116 us); the same bits every way.
+// three 16-row blocks; 64-row workgroups since, below); the same bits
+// either way.
 constexpr int64_t kSpreadMaxRowsLeft = 32;
 
 // The chained 128-row block tiling can give the blocks past one per CU to
@@ -217,13 +217,11 @@ Launch choose_launch(const MemberPlan *mp, int n, int64_t M) {
   const bool wide = mt == 16 || (mt == -1 && M > 128 && long_chains);
   int mid_chained = -1;
   bool mid_spread = false;
-  bool block64 = false;
   const bool left_fits = block_left_fits(mp, n, blocks, ncu);
   if (mt == 16) {
     mt = 8;
   } else if (mt == -1 && M > kSpreadMaxRowsLeft && M <= 128 && left_fits && !all_single) {
-    block64 = M <= 64;
-    mt = block64 ? 4 : 8;
+    mt = 8;
     mid_chained = 1;
   } else if (mt == -1 && M > 16 && M <= kSpreadMaxRows && sp_own > 0) {
     mt = 1;
@@ -286,11 +284,18 @@ Launch choose_launch(const MemberPlan *mp, int n, int64_t M) {
            : spread    ? exl3::kSpread16
            : mt == 1 ? (L.chained ? exl3::kChain16x8 : halves ? exl3::kChain16H : exl3::kChain16)
            : mt == 2 ? exl3::kChain32
-           : block64 ? exl3::kBlock64
            : mt == 4 ? exl3::kNtile64
            : wide && L.chained ? exl3::kWide128
            : !L.chained && long_chains ? exl3::kTile128
                      : exl3::kBlock128;
+  // Automatic chained 128-row block tiles of at most 64 rows run 64-row
+  // workgroups: half the MFMAs, the same bits (3-bit {gate, up} pair: MLP at
+  // 33-64 rows 112-129 -> 98-116 us; 6-bit head at 49 / 64 rows 406-411 /
+  // 384-394 -> 358-361 / 328-345 us)
+  if (L.kernel == exl3::kBlock128 && L.chained && M <= 64 && g_hooks.m_tiles == -1) {
+    L.kernel = exl3::kBlock64;
+    L.m_tiles = 4;
+  }
   L.exchange = !L.chained || (spread && L.left_blocks > 0);
   // The 2 x 2 tiling's exchange adds 64 KB partials: its last arriving
   // workgroup would make one memory round trip per split for the whole
