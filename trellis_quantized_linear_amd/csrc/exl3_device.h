@@ -1153,7 +1153,13 @@ void linear_chain_kernel(const LinearArgs a) {
   // wave index as a scalar: everything derived from it (split, chunk,
   // buffer offsets) stays in SGPRs
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int bid = blockIdx.x;
+  // Exchanged: workgroups are dealt to the 8 XCDs in turn, each XCD taking a
+  // contiguous range of (row block, block, split group), so a block's split
+  // groups share an XCD and its L2 (the decode step at 16 / 1 rows 44.0-44.3
+  // -> 43.3-43.6 / 39.8-40.1 -> 38.5-38.7 us, view B 18.2-18.3 -> 17.5-17.6
+  // us; the same bytes, the exchange stays agent-scope)
+  const int T = a.total_wgs, xcd = blockIdx.x & 7;
+  const int bid = CHAINED ? (int)blockIdx.x : xcd * (T >> 3) + min(xcd, T & 7) + (int)(blockIdx.x >> 3);
   int j = 0;
   if (a.n_members > 1 && bid >= a.m[1].wg_begin) j = 1;
   if (a.n_members > 2 && bid >= a.m[2].wg_begin) j = 2;
