@@ -1186,14 +1186,16 @@ void linear_chain_kernel(const LinearArgs a) {
   char *wlds = lds + wave * SB::kWave;
 
   const int sw = wave / (8 / CT), half = wave % (8 / CT);   // the wave's split in the workgroup, its columns
-  const ChainCtx<BITS, MT, CT> x = chain_ctx<BITS, MT, CT>(m, M, K, nb, row_base, lane, false, half);
+  // Xr chunk-major (the column-halves form, one row block) or row-major
+  const bool cm = CT == 4 && a.xr_chunk_major != 0;
+  const ChainCtx<BITS, MT, CT> x = chain_ctx<BITS, MT, CT>(m, M, K, nb, row_base, lane, cm, half);
   const int c = lane & 15, g = lane >> 4;
   // one row block (row_base == 0); the 8-wave chained form (weights of many
   // blocks, where a rotation launch costs little) would spill with the fused
   // prologue
   const bool fused = (W != 8 || CT == 4) && a.x != nullptr;
   __shared__ int s_clear;
-  if (fused) rot_produce<4 * MT>(a, wave, lane, false);
+  if (fused) rot_produce<4 * MT>(a, wave, lane, cm);
 
   const int s_first = CHAINED ? sw : SPW * sg + sw;
   const int rounds = CHAINED ? (S + SPW - 1) / SPW : 1;
@@ -1209,7 +1211,7 @@ void linear_chain_kernel(const LinearArgs a) {
       constexpr int P = (W == 8 && SB::kLoads > 2) ? 2 : ChainDepth<MT>::P;
       const int c0 = (int)(((int64_t)s * C) / S), c1 = (int)(((int64_t)(s + 1) * C) / S);
       run_chain<BITS, MT, P, CT, POL>(acc, c0, c1, wlds, x, fused,
-                             [&] { rot_wait<4 * MT>(a, j, c0 >> 2, (c1 - 1) >> 2, lane, false); });
+                             [&] { rot_wait<4 * MT>(a, j, c0 >> 2, (c1 - 1) >> 2, lane, cm); });
     }
     if constexpr (CHAINED) {
       // fold this round's chains into the running sum in split order
