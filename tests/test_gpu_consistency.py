@@ -400,3 +400,30 @@ def test_split_fold_launch_equals_the_chained_fold():
                 assert form == ("linear_tile_kernel<4, false>" if chained == 0 else "linear_block_kernel<4, true>"), form
             assert np.array_equal(ys[0], ys[1]), (M, S)
             assert int(ws.counters().abs().sum()) == 0, (M, S)
+
+
+@pytest.mark.parametrize("N", [384, 640, 1152])
+def test_exchanged_launch_with_blocks_across_xcd_ranges(N):
+    """Exchanged 16- and 32-row launches deal their workgroups to the XCDs
+    in contiguous ranges; with 3, 5 or 9 blocks a block's split groups fall
+    into two ranges. Every exchanged form (one split per wave, the column
+    halves, 32-row tiles) gives the bytes of the chained form, at 1, 16 and
+    17 rows, and leaves the counters at zero."""
+    K = 5120
+    L = G.layer("xcd-ranges", f"w{N}", K, N, 4)
+    w = G.upload(L)
+    xd = G.dev_bf16(G.xbits("xcd-ranges", 32, K))
+    ws = ex().Workspace().reserve([w], 32)
+    for M in (1, 16, 17):
+        ys = {}
+        for mt, chained in ((1, 1), (1, 0), (1, 3), (2, 0), (2, 1)):
+            if M > 16 and mt == 1:
+                continue
+            ex().exl3_test_force(mt, chained, 0)
+            ws.reserve([w], M)
+            ys[(mt, chained)] = G.host_u16(G.run(w, xd, M=M, ws=ws, tag=f"N={N} M={M} m_tiles={mt} chained={chained}"))
+            ex().exl3_test_force(-1, -1, 0)
+        ref = ys[(1, 1)] if M <= 16 else ys[(2, 1)]
+        for k, y in ys.items():
+            assert np.array_equal(y[:M], ref[:M]), (N, M, k)
+        assert int(ws.counters().abs().sum()) == 0, (N, M)
