@@ -288,8 +288,9 @@ def test_split_exchange_stress():
     assert int(ws.counters().abs().sum()) == 0
 
 
-TWO_PHASE = [(1, (-1, -1, 0)), (16, (-1, -1, 0)), (16, (1, 2, 4)), (40, (-1, -1, 0)), (64, (-1, -1, 0)),
-             (100, (-1, -1, 0)), (128, (-1, -1, 0)), (128, (8, 0, 0)), (200, (-1, -1, 0))]
+TWO_PHASE = [(1, (-1, -1, 0)), (16, (-1, -1, 0)), (16, (1, 2, 4)), (7, (1, 3, 0)), (16, (1, 0, 0)),
+             (40, (-1, -1, 0)), (64, (-1, -1, 0)), (100, (-1, -1, 0)), (128, (-1, -1, 0)), (128, (8, 0, 0)),
+             (200, (-1, -1, 0))]
 
 
 @pytest.mark.parametrize("M,force", TWO_PHASE)
@@ -297,9 +298,10 @@ def test_two_phase_calls_equal_the_group_call(M, force):
     """exl3_rotate then exl3_linear_rotated give the bytes of one
     exl3_linear_group call: the rotation writes Xr in the layout the linear
     launch of that row count reads (chunk-major for the spread launch, forced
-    here with 4 splits at 16 rows, and for the 128-row tilings at 100, 128
-    and 200 rows, chained and exchanged; row-major for the other 16- to
-    64-row launches)."""
+    here with 4 splits at 16 rows, for the exchanged column halves, forced at
+    7 rows, and for the 128-row tilings at 100, 128 and 200 rows, chained and
+    exchanged; row-major for the other 16- to 64-row launches, such as the
+    exchanged 16-row form forced at 16 rows)."""
     torch = G.torch_mod()
     K = 5120
     layers = [G.layer("two-phase", n, K, N, 3) for n, N in (("gate", 2048), ("up", 2048), ("k", 1024))]
