@@ -58,11 +58,11 @@ struct LinearArgs {
   int32_t spin_limit;         // polls of an unwritten chunk's flag before a wave rotates it itself
 };
 
-// Workgroups of the split-fold launch that follows a 128-row exchanged
-// launch: one per (member, row block, block, 16-row tile).
+// Workgroups (one wave each) of the split-fold launch: one per (member, row
+// block, block, 16-row tile, group of 4 rows).
 inline int64_t split_fold_wgs(const LinearArgs &a) {
   int64_t n = 0;
-  for (int j = 0; j < a.n_members; ++j) n += (int64_t)a.row_blocks * a.m[j].n_blocks * 8;
+  for (int j = 0; j < a.n_members; ++j) n += (int64_t)a.row_blocks * a.m[j].n_blocks * 32;
   return n;
 }
 

@@ -60,32 +60,36 @@ __global__ __launch_bounds__(kThreads) void rot_kernel(const RotArgs a) {
 // ------------------------------------------------------------ split fold
 //
 // After a 128-row exchanged launch that only stored its split partials
-// (LinearArgs::fold_launch): one workgroup per (member, row block, block,
-// 16-row tile) adds that tile's S partials in split order, z = P0, then
-// z + P1, ... (the same fp32 additions, in the same order, as the linear
-// launch's last arriving workgroup would make), and runs the epilogue of its
-// 16 rows. A tile is 16 rows x 128 columns, 8 KB per split in the fragment
-// layout; thread x owns fragments x and x + 256 of its 512 and issues the
-// loads of every split before the first addition.
-__global__ __launch_bounds__(kThreads) void split_fold_kernel(const LinearArgs a) {
+// (LinearArgs::fold_launch), and for the left blocks of the chained block
+// tiling: one wave per (member, row block, block, 16-row tile, group of 4
+// rows) adds those rows' S partials in split order, z = P0, then z + P1,
+// ... (the same fp32 additions, in the same order, as a linear launch's
+// last arriving workgroup would make), and runs the epilogue of its 4
+// rows. A 16-row tile is 512 fragments of 4 rows x 1 column, 8 KB per split
+// in the fragment layout; the 128 fragments of rows 4q .. 4q + 3 are
+// fragments t * 64 + 16 q + c (column tile t, column c); lane l loads
+// column c = l % 16 of column tiles l / 16 and l / 16 + 4, every split's
+// loads before the first addition. One-wave workgroups spread the loads
+// over the CUs (the down projection's 320 tiles are 1280 waves).
+__global__ __launch_bounds__(64) void split_fold_kernel(const LinearArgs a) {
   constexpr int kMaxSplits = 16;
   const int RB = a.row_blocks;
   int64_t local = blockIdx.x;
   int j = 0;
-  while (j + 1 < a.n_members && local >= (int64_t)RB * a.m[j].n_blocks * 8) {
-    local -= (int64_t)RB * a.m[j].n_blocks * 8;
+  while (j + 1 < a.n_members && local >= (int64_t)RB * a.m[j].n_blocks * 32) {
+    local -= (int64_t)RB * a.m[j].n_blocks * 32;
     ++j;
   }
   const MemberArgs &m = a.m[j];
-  const int per_rb = m.n_blocks * 8;
+  const int per_rb = m.n_blocks * 32;
   const int rb = (int)(local / per_rb);
   const int rem = (int)(local - (int64_t)rb * per_rb);
-  const int nb = rem >> 3, mt = rem & 7;
-  const int row0 = 128 * rb + 16 * mt;
+  const int nb = rem >> 5, mt = (rem >> 2) & 7, q = rem & 3;
+  const int row0 = 128 * rb + 16 * mt + 4 * q;
   if (row0 >= a.M) return;                                 // uniform
   const int S = m.splits;
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x;
+  const int c = lane & 15, t0 = lane >> 4;
   const int col0 = nb * kBlockCols;
 
   u32x4 v[kMaxSplits][2];
@@ -96,7 +100,7 @@ __global__ __launch_bounds__(kThreads) void split_fold_kernel(const LinearArgs a
 #pragma unroll
       for (int e = 0; e < 2; ++e)
         v[s][e] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                rp, 16 * (int)(threadIdx.x + e * kThreads), 0, kAgentScope));
+                                                rp, 16 * ((t0 + 4 * e) * 64 + 16 * q + c), 0, kAgentScope));
     }
   }
   f32x4 z[2];
@@ -108,17 +112,14 @@ __global__ __launch_bounds__(kThreads) void split_fold_kernel(const LinearArgs a
 #pragma unroll
       for (int e = 0; e < 2; ++e) z[e] = z[e] + __builtin_bit_cast(f32x4, v[s][e]);
 
-  __shared__ __attribute__((aligned(16))) float zrow[16 * 132];
+  __shared__ __attribute__((aligned(16))) float zrow[4 * 132];
 #pragma unroll
-  for (int e = 0; e < 2; ++e) {
-    const int f = threadIdx.x + e * kThreads;              // column tile f / 64, lane f % 64
-    const int fl = f & 63, ft = f >> 6;
+  for (int e = 0; e < 2; ++e)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) zrow[(4 * (fl >> 4) + q) * 132 + 16 * ft + (fl & 15)] = z[e][q];
-  }
+    for (int r = 0; r < 4; ++r) zrow[r * 132 + 16 * (t0 + 4 * e) + c] = z[e][r];
   const EpiCols ec = epi_cols(m, col0, lane);
   __syncthreads();
-  if (row0 + 4 * wave < a.M) epilogue_rows_lds<1>(zrow + 4 * wave * 132, 132, ec, lane, m, col0, row0 + 4 * wave, a.M);
+  epilogue_rows_lds<1>(zrow, 132, ec, lane, m, col0, row0, a.M);
 }
 
 // ------------------------------------------------------------ test hooks
@@ -215,7 +216,7 @@ int launch_split_fold(const LinearArgs &a, void *stream) {
     if (a.m[j].splits < 1 || a.m[j].splits > 16) return (int)hipErrorInvalidValue;
   if (wgs <= 0 || wgs >= (int64_t(1) << 31)) return (int)hipErrorInvalidValue;
   (void)hipGetLastError();
-  hipLaunchKernelGGL(split_fold_kernel, dim3((unsigned)wgs), dim3(kThreads), 0, (hipStream_t)stream, a);
+  hipLaunchKernelGGL(split_fold_kernel, dim3((unsigned)wgs), dim3(64), 0, (hipStream_t)stream, a);
   return (int)hipGetLastError();
 }
 
