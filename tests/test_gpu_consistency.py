@@ -379,18 +379,18 @@ def test_64_row_block_tiling_equals_the_128_row_one(what, K, Ns, bits, rows):
 
 
 def test_split_fold_launch_equals_the_chained_fold():
-    """Down-shaped weight (K 17408: long splits) at 100 and 128 rows: the
-    exchanged 2 x 2 tiling whose partials the split-fold launch adds gives
-    the bytes of the chained 128-row block tiling (every split folded in one
-    workgroup); with a forced plan of 17 splits the tiling folds in its last
-    arriving workgroup instead, again byte for byte the chained form.
-    Counters zero afterwards."""
+    """Down-shaped weight (K 17408: long splits) at 100, 128 and 200 rows
+    (two row blocks): the exchanged 2 x 2 tiling whose partials the
+    split-fold launch adds gives the bytes of the chained 128-row block
+    tiling (every split folded in one workgroup); with a forced plan of 17
+    splits the tiling folds in its last arriving workgroup instead, again
+    byte for byte the chained form. Counters zero afterwards."""
     K, N = 17408, 1024
     L = G.layer("split-fold", "down", K, N, 4)
     w = G.upload(L)
-    xd = G.dev_bf16(G.xbits("split-fold", 128, K))
-    ws = ex().Workspace().reserve([w], 128)
-    for M in (100, 128):
+    xd = G.dev_bf16(G.xbits("split-fold", 200, K))
+    ws = ex().Workspace().reserve([w], 200)
+    for M in (100, 128, 200):
         for S in (0, 17):
             ys = {}
             for chained in (0, 1):
