@@ -19,10 +19,10 @@ output is its own single-weight launch's, which the oracle defines).
   M - 1 byte for byte against one-row calls).
 * The same pair at 40 rows at widths 2 and 4-8 (the 64-row block tiling
   with its left blocks at every width).
-* A stress of the relaxed split-K exchange on that headline launch: 10^4
-  group calls at 16 rows, bytes compared every 100 calls, counters zero at
-  the end (PR #1475, "What this changes": the last arriver resets its
-  counter).
+* A stress of the relaxed split-K exchange on that headline launch and on
+  the {q, k, v} group's exchanged launch: 10^4 group calls each at 16 rows,
+  bytes compared every 100 calls, counters zero at the end (PR #1475, "What
+  this changes": the last arriver resets its counter).
 """
 
 import numpy as np
@@ -127,17 +127,22 @@ def test_gate_up_block_tiling_left_blocks_every_width_vs_oracle(bits):
     assert ex().exl3_test_last_form() == f"linear_block64_kernel<{bits}>"
 
 
-def test_gate_up_spread_exchange_stress():
-    """10^4 calls of the headline launch ({gate, up}, M = 16), bytes compared
-    with the first call every 100 calls (stops at the first mismatch), split
-    counters zero at the end."""
+@pytest.mark.parametrize("names,form", [(("gate", "up"), "linear_spread_kernel<4>"),
+                                        (("q", "k", "v"), "linear_chain_kernel<4, 1, false, 8, 4, 2>")])
+def test_decode_group_exchange_stress(names, form):
+    """10^4 calls of each decode-row group launch at M = 16: {gate, up} (the
+    headline spread launch, its left blocks exchanged) and {q, k, v} (the
+    exchanged column halves, a block's split groups dealt to one XCD's
+    range), bytes compared with the first call every 100 calls (stops at the
+    first mismatch), split counters zero at the end."""
     torch = G.torch_mod()
-    layers = [G.layer("stress-gu", n, K, COLS[n], 4) for n in ("gate", "up")]
+    layers = [G.layer("stress-gu" if len(names) == 2 else "stress-qkv", n, K, COLS[n], 4) for n in names]
     ws_ = [G.upload(L) for L in layers]
-    xd = G.dev_bf16(G.xbits("stress-gu", 16, K))
+    xd = G.dev_bf16(G.xbits("stress-gu" if len(names) == 2 else "stress-qkv", 16, K))
     ws = ex().Workspace().reserve(ws_, 16)
     ref = G.run_group(ws_, xd, ws=ws, tag="stress reference")
     torch.cuda.synchronize()
+    assert ex().exl3_test_last_form() == form
     ys = [[G.empty_y(16, L.N) for L in layers] for _ in range(100)]
     for batch in range(100):
         if batch % 20 == 0:
