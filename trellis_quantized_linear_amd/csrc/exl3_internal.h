@@ -74,6 +74,8 @@ constexpr int64_t kMaxFusedFlags = 1024;
 // Rotation launches of at least this many (4 rows, 128-chunk) items per
 // member read X once for all members (a thousand rows at K = 5120).
 constexpr int64_t kRotSharedItems = 10240;
+// Rotation launches of at most this many pieces run one wave per workgroup.
+constexpr int64_t kRotOneWaveItems = 4096;
 
 struct RotArgs {
   const uint16_t *x;          // bf16 [M][ldx]

@@ -32,7 +32,7 @@ namespace {
 __global__ __launch_bounds__(kThreads) void rot_kernel(const RotArgs a) {
   const int lane = threadIdx.x & 63;
   const int c = lane & 15, g = lane >> 4;
-  const int64_t item = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
+  const int64_t item = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
   const int kc = a.K >> 7;
   const int quads = (a.M + 3) >> 2;
   const int64_t per_member = (int64_t)quads * kc;
@@ -204,9 +204,13 @@ int launch_rot(const RotArgs &a_in, void *stream) {
   const int64_t per_member = (int64_t)((a.M + 3) / 4) * (a.K / 128);
   a.shared_x = a.n_members > 1 && per_member >= kRotSharedItems ? 1 : 0;
   const int64_t items = per_member * (a.shared_x ? 1 : a.n_members);
-  const int64_t wgs = (items + kWaves - 1) / kWaves;
+  // One-wave workgroups up to kRotOneWaveItems pieces (the decode step at 16
+  // / 1 rows 43.4-43.6 -> 43.2-43.3 / 38.8-39.6 -> 38.2 us), 4-wave ones for
+  // prompt rows.
+  const int wpw = items <= kRotOneWaveItems ? 1 : kWaves;
+  const int64_t wgs = (items + wpw - 1) / wpw;
   (void)hipGetLastError();
-  hipLaunchKernelGGL(rot_kernel, dim3((unsigned)wgs), dim3(kThreads), 0, (hipStream_t)stream, a);
+  hipLaunchKernelGGL(rot_kernel, dim3((unsigned)wgs), dim3(64 * wpw), 0, (hipStream_t)stream, a);
   return (int)hipGetLastError();
 }
 
