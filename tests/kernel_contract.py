@@ -47,7 +47,10 @@ FORMS = {
                                           (256, [384], 300, ""), (256, [1024, 256, 256], 200, "")]),
     # 64-row block tiling: a few more blocks than CUs at 33-64 rows (left blocks as single splits)
     "linear_block64_kernel<{b}>": (2, [(256, [34816], 33, ""), (256, [17408, 17408], 64, "")]),
-    "linear_tile_kernel<{b}, false>": (3, [(16384, [128], 97, ""), (16384, [128, 256], 64, "")]),
+    # exchanged 2 x 2 tiles of 64 rows (2 waves), partials added by the split-fold launch; the
+    # 128-row form (4 waves) is reached only through exl3_test_force now
+    "linear_tile64_kernel<{b}>": (3, [(16384, [128], 97, ""), (16384, [128, 256], 64, ""), (17408, [5120], 49, ""),
+                                     (17408, [5120], 128, "")]),
     # prompt rows of long-split weights (down): 128 rows x 2 blocks (the last pair of an odd count: 1)
     "linear_wide_kernel<{b}>": (1, [(16384, [128], 129, ""), (16384, [384], 300, ""), (17408, [256, 128], 200, "")]),
     # opt-in single-chain prompt tiles (other bits than the rest, by design)

@@ -382,9 +382,10 @@ def test_split_fold_launch_equals_the_chained_fold():
     """Down-shaped weight (K 17408: long splits) at 100, 128 and 200 rows
     (two row blocks): the exchanged 2 x 2 tiling whose partials the
     split-fold launch adds gives the bytes of the chained 128-row block
-    tiling (every split folded in one workgroup); with a forced plan of 17
-    splits the tiling folds in its last arriving workgroup instead, again
-    byte for byte the chained form. Counters zero afterwards."""
+    tiling (every split folded in one workgroup), in 128-row tiles (forced)
+    and in the automatic 64-row tiles; with a forced plan of 17 splits the
+    tiling folds in its last arriving workgroup instead, again byte for byte
+    the chained form. Counters zero afterwards."""
     K, N = 17408, 1024
     L = G.layer("split-fold", "down", K, N, 4)
     w = G.upload(L)
@@ -402,6 +403,12 @@ def test_split_fold_launch_equals_the_chained_fold():
                 assert form == ("linear_tile_kernel<4, false>" if chained == 0 else "linear_block_kernel<4, true>"), form
             assert np.array_equal(ys[0], ys[1]), (M, S)
             assert int(ws.counters().abs().sum()) == 0, (M, S)
+            if S == 0 and M <= 128:
+                # the automatic launch: the same tiling in 64-row tiles of 2 waves
+                ws.reserve([w], M)
+                y64 = G.host_u16(G.run(w, xd, M=M, ws=ws, tag=f"split fold M={M} automatic"))
+                assert ex().exl3_test_last_form() == "linear_tile64_kernel<4>"
+                assert np.array_equal(y64, ys[1]), M
 
 
 @pytest.mark.parametrize("N", [384, 640, 1152])

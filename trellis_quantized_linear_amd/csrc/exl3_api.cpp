@@ -305,6 +305,15 @@ Launch choose_launch(const MemberPlan *mp, int n, int64_t M) {
   int32_t max_splits = 0;
   for (int j = 0; j < n; ++j) max_splits = std::max(max_splits, mp[j].splits);
   L.fold_launch = L.kernel == exl3::kTile128 && !L.chained && max_splits <= 16;
+  // ... in 64-row tiles of 2 waves: the down projection's 640 128-row tiles
+  // left 128 CUs with three workgroups and 128 with two (the launch 34 us,
+  // its 2-workgroup CUs done at 26 us); 64-row tiles are 2.5 or 5 per CU,
+  // and at up to 64 rows no wave computes masked rows
+  if (L.fold_launch && g_hooks.m_tiles == -1) {
+    L.kernel = exl3::kTile64;
+    L.m_tiles = 4;
+    L.row_blocks = (M + 63) / 64;
+  }
   // The chained 128-row block tiling over one row block with a few more
   // blocks than CUs ({gate, up} at 33-128 rows: 272 blocks on 256 CUs): the
   // blocks past one per CU would run as second workgroups on a few CUs and
@@ -577,7 +586,7 @@ int run_group(int32_t n_members, const exl3_weight_t *const *w, const void *x, i
   // Chunk offsets are 32-bit: chunk-major needs 2 K M < 2^31, which every
   // accepted call meets (check_group).
   const bool tile_cm = (L.kernel == exl3::kTile128 || L.kernel == exl3::kBlock128 || L.kernel == exl3::kWide128 ||
-                        L.kernel == exl3::kQuad128 || L.kernel == exl3::kBlock64) &&
+                        L.kernel == exl3::kQuad128 || L.kernel == exl3::kBlock64 || L.kernel == exl3::kTile64) &&
                        2 * K * M < (int64_t(1) << 31);
   // The 16-row column-halves launch ({q, k, v} at decode rows) reads its
   // 16 rows of a chunk as 8 whole lines instead of 16 half-used ones (the
@@ -586,6 +595,7 @@ int run_group(int32_t n_members, const exl3_weight_t *const *w, const void *x, i
   ra.chunk_major = L.kernel == exl3::kSpread16 || tile_cm || halves_cm ? 1 : 0;
   la.xr_chunk_major = tile_cm || halves_cm ? 1 : 0;
   la.fold_launch = L.fold_launch ? 1 : 0;
+  la.fold_tiles = L.kernel == exl3::kTile64 ? 4 : 8;       // partials of 64- or 128-row blocks
   la.n_members = n_members;
   la.M = (int32_t)M;
   la.K = (int32_t)K;

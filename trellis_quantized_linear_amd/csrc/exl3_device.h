@@ -1336,36 +1336,47 @@ void linear_chain_kernel(const LinearArgs a) {
 // 4 column tiles from the staged words and issues 16 MFMAs. Chains, their
 // fold in split order and the epilogue are those of every other tiling.
 
-template <int BITS>
+// RH row halves of 64 rows: 2 (the 128-row tile, 4 waves) or 1 (the 64-row
+// tile, 2 waves).
+template <int BITS, int RH = 2>
 struct TileLds {
   static constexpr int kArow = 80;                         // bytes per staged A row
-  static constexpr int kA = 128 * kArow;
+  static constexpr int kA = 64 * RH * kArow;
   static constexpr int kBuf = kA + Stream<BITS>::kSlot;    // one chunk: A tile + B words
+  static constexpr int kWaves = 2 * RH;
+  static constexpr int kPieces = (Stream<BITS>::kLoads + kWaves - 1) / kWaves;   // B loads per wave
 };
 
+template <int NB>
 struct TileStage {
   u32x4 a[2];                                              // this wave's 2 A loads (32 rows)
-  u32x4 b;                                                 // this wave's B load
+  u32x4 b[NB];                                             // this wave's B loads
 };
 
-__device__ __forceinline__ void load_tile_stage(TileStage &st, __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
-                                                const uint32_t (&voff_a)[2], int a_step, uint32_t voff_b, int chunk,
-                                                int chunk_bytes) {
+template <int NB>
+__device__ __forceinline__ void load_tile_stage(TileStage<NB> &st, __amdgpu_buffer_rsrc_t ra,
+                                                __amdgpu_buffer_rsrc_t rb, const uint32_t (&voff_a)[2], int a_step,
+                                                const uint32_t (&voff_b)[NB], int chunk, int chunk_bytes) {
   st.a[0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, (int)voff_a[0], chunk * a_step, 0));
   st.a[1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, (int)voff_a[1], chunk * a_step, 0));
-  st.b = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, (int)voff_b, chunk * chunk_bytes, 0));
+#pragma unroll
+  for (int i = 0; i < NB; ++i)
+    st.b[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, (int)voff_b[i], chunk * chunk_bytes, 0));
 }
 
-template <int BITS>
-__device__ __forceinline__ void tile_stage_to_lds(const TileStage &st, char *buf, const uint32_t (&a_wr)[2],
-                                                  uint32_t b_wr, uint32_t b_wrap) {
+template <int BITS, int RH, int NB>
+__device__ __forceinline__ void tile_stage_to_lds(const TileStage<NB> &st, char *buf, const uint32_t (&a_wr)[2],
+                                                  const uint32_t (&b_wr)[NB], const uint32_t (&b_wrap)[NB]) {
   *(u32x4 *)(buf + a_wr[0]) = st.a[0];
   *(u32x4 *)(buf + a_wr[1]) = st.a[1];
-  *(u32x4 *)(buf + TileLds<BITS>::kA + b_wr) = st.b;
-  *(uint32_t *)(buf + TileLds<BITS>::kA + b_wrap) = st.b[0];
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    *(u32x4 *)(buf + TileLds<BITS, RH>::kA + b_wr[i]) = st.b[i];
+    *(uint32_t *)(buf + TileLds<BITS, RH>::kA + b_wrap[i]) = st.b[i][0];
+  }
 }
 
-template <int BITS>
+template <int BITS, int RH>
 __device__ __forceinline__ void compute_tile_chunk(const char *buf, const uint32_t (&a_rd)[4], uint32_t b_rd,
                                                    uint32_t shift, const CbConst &cb, f32x4 (&acc)[4][4]) {
   constexpr int ND = BitsTraits<BITS>::kDwords;
@@ -1374,7 +1385,7 @@ __device__ __forceinline__ void compute_tile_chunk(const char *buf, const uint32
   for (int mt = 0; mt < 4; ++mt) af[mt] = __builtin_bit_cast(half8, *(const u32x4 *)(buf + a_rd[mt]));
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const uint32_t *q = (const uint32_t *)(buf + TileLds<BITS>::kA + b_rd + i * Stream<BITS>::kStride);
+    const uint32_t *q = (const uint32_t *)(buf + TileLds<BITS, RH>::kA + b_rd + i * Stream<BITS>::kStride);
     uint32_t w[ND];
 #pragma unroll
     for (int d = 0; d < ND; ++d) w[d] = q[d];
@@ -1385,16 +1396,17 @@ __device__ __forceinline__ void compute_tile_chunk(const char *buf, const uint32
   }
 }
 
-// Exchanged (one split per workgroup, about 165 VGPRs): three workgroups per
-// CU, so that the down projection's 640 workgroups at 49-128 rows run in one
-// round instead of 1.25 (-5 to -9 %); chained (about 230 VGPRs): two.
-template <int BITS, bool CHAINED>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(CHAINED ? 2 : 3, CHAINED ? 2 : 3)))
-void linear_tile_kernel(const LinearArgs a) {
+template <int BITS, bool CHAINED, int RH>
+__device__ __forceinline__ void tile_body(const LinearArgs &a) {
   using SB = Stream<BITS>;
-  using TL = TileLds<BITS>;
-  constexpr int R = 128;
-  constexpr int P = 4;                                     // register stages (chunks in flight)
+  using TL = TileLds<BITS, RH>;
+  constexpr int W = TL::kWaves;
+  constexpr int NB = TL::kPieces;
+  constexpr int R = 64 * RH;
+  constexpr int RT = 4 * RH;                               // 16-row tiles of a workgroup
+  // register stages (chunks in flight; even, for the two LDS buffers): 2
+  // where a wave stages two word pieces (64-row tiles above 4 bits)
+  constexpr int P = NB > 1 ? 2 : 4;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wr = wave >> 1, wc = wave & 1;
@@ -1416,7 +1428,8 @@ void linear_tile_kernel(const LinearArgs a) {
   const int col0 = nb * kBlockCols;
 
   constexpr int kStage = 2 * TL::kBuf;
-  constexpr int kEpi = 64 * 132 * 4;
+  constexpr int PR = 16 * W;                               // rows per epilogue pass
+  constexpr int kEpi = PR * 132 * 4;
   __shared__ __attribute__((aligned(16))) char lds[kStage > kEpi ? kStage : kEpi];
 
   // Xr row-major or chunk-major (each chunk's M rows contiguous, 64 bytes a row)
@@ -1427,8 +1440,8 @@ void linear_tile_kernel(const LinearArgs a) {
   const int c = lane & 15, g = lane >> 4;
 
   // staging: wave w loads A rows 32w .. 32w+31 (16 per 128-bit load, 4 lanes
-  // a row) and, if w < kLoads, the w-th 1 KB of the chunk's words (other
-  // waves and lanes past the chunk load its first bytes into the dump)
+  // a row) and the 1 KB pieces w, w + W, ... of the chunk's words (pieces
+  // and lanes past the chunk load its first bytes into the dump)
   uint32_t voff_a[2], a_wr[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
@@ -1437,13 +1450,18 @@ void linear_tile_kernel(const LinearArgs a) {
     voff_a[i] = row < M ? (uint32_t)(row * (cm ? 64 : 2 * K) + 16 * (lane & 3)) : kOutOfRange;
     a_wr[i] = (uint32_t)(r * TL::kArow + 16 * (lane & 3));
   }
-  const int boff = 1024 * wave + 16 * lane;
-  const bool bvalid = wave < SB::kLoads && boff < SB::kChunkBytes;
-  const int tau_w = boff / (32 * BITS), w_in = boff % (32 * BITS);
-  const uint32_t voff_b = bvalid ? (uint32_t)boff : 0u;
-  const uint32_t b_wr = bvalid ? (uint32_t)(tau_w * SB::kStride + w_in) : (uint32_t)(16 * SB::kStride);
-  const uint32_t b_wrap =
-      bvalid ? (uint32_t)(tau_w * SB::kStride + 32 * BITS + (w_in == 0 ? 0 : 4)) : (uint32_t)(16 * SB::kStride);
+  uint32_t voff_b[NB], b_wr[NB], b_wrap[NB];
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    const int piece = wave + W * i;
+    const int boff = 1024 * piece + 16 * lane;
+    const bool bvalid = piece < SB::kLoads && boff < SB::kChunkBytes;
+    const int tau_w = boff / (32 * BITS), w_in = boff % (32 * BITS);
+    voff_b[i] = bvalid ? (uint32_t)boff : 0u;
+    b_wr[i] = bvalid ? (uint32_t)(tau_w * SB::kStride + w_in) : (uint32_t)(16 * SB::kStride);
+    b_wrap[i] =
+        bvalid ? (uint32_t)(tau_w * SB::kStride + 32 * BITS + (w_in == 0 ? 0 : 4)) : (uint32_t)(16 * SB::kStride);
+  }
   // reading: A fragments of m-tiles 4wr..4wr+3, B words of column tiles 4wc..4wc+3
   uint32_t a_rd[4];
 #pragma unroll
@@ -1469,21 +1487,21 @@ void linear_tile_kernel(const LinearArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[mt][i] = z[mt][i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  TileStage st[P];
+  TileStage<NB> st[P];
 #pragma unroll
   for (int p = 0; p < P; ++p) {
-    load_tile_stage(st[p], ra, rbuf, voff_a, a_step, voff_b, min(cb + p, last), SB::kChunkBytes);
+    load_tile_stage<NB>(st[p], ra, rbuf, voff_a, a_step, voff_b, min(cb + p, last), SB::kChunkBytes);
     __builtin_amdgcn_sched_barrier(0);
   }
-  tile_stage_to_lds<BITS>(st[0], lds, a_wr, b_wr, b_wrap);
+  tile_stage_to_lds<BITS, RH, NB>(st[0], lds, a_wr, b_wr, b_wrap);
 
   // one step: chunk cc from LDS buffer `cur`; chunk cc+1 is staged into the
   // other buffer first; the register stage of chunk cc reloads chunk cc+P
-  auto step = [&](int cc, char *cur, char *nxt, TileStage &mine, TileStage &next, bool has_next) {
+  auto step = [&](int cc, char *cur, char *nxt, TileStage<NB> &mine, TileStage<NB> &next, bool has_next) {
     __syncthreads();
-    if (has_next) tile_stage_to_lds<BITS>(next, nxt, a_wr, b_wr, b_wrap);
-    load_tile_stage(mine, ra, rbuf, voff_a, a_step, voff_b, min(cc + P, last), SB::kChunkBytes);
-    compute_tile_chunk<BITS>(cur, a_rd, b_rd, shift, cbc, acc);
+    if (has_next) tile_stage_to_lds<BITS, RH, NB>(next, nxt, a_wr, b_wr, b_wrap);
+    load_tile_stage<NB>(mine, ra, rbuf, voff_a, a_step, voff_b, min(cc + P, last), SB::kChunkBytes);
+    compute_tile_chunk<BITS, RH>(cur, a_rd, b_rd, shift, cbc, acc);
     if (cc + 1 == bnd) {                                   // chain s complete (uniform)
       if constexpr (CHAINED) {
 #pragma unroll
@@ -1512,12 +1530,12 @@ void linear_tile_kernel(const LinearArgs a) {
     if (p < r)
       step(cb + i + p, lds + (p % 2) * TL::kBuf, lds + ((p + 1) % 2) * TL::kBuf, st[p], st[(p + 1) % P], p + 1 < r);
 
-  float *zbuf = (float *)lds;                              // [64][132]: 64 rows per epilogue pass
+  float *zbuf = (float *)lds;                              // [PR][132]: PR rows per epilogue pass
   const EpiCols ec = epi_cols(m, col0, lane);
 
   if constexpr (!CHAINED) {
     // split sg's partial in the fragment layout, then the counter exchange
-    const __amdgpu_buffer_rsrc_t rp = make_rsrc(partial_frag(m, sg, rb, nb, a.row_blocks, 8), 8 * 8 * 1024);
+    const __amdgpu_buffer_rsrc_t rp = make_rsrc(partial_frag(m, sg, rb, nb, a.row_blocks, RT), RT * 8 * 1024);
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
@@ -1544,7 +1562,7 @@ void linear_tile_kernel(const LinearArgs a) {
     // rows past M hold stale bytes (in bounds: whole 128-row blocks) that no
     // row of the epilogue uses.
     for (int sp = 0; sp < S; ++sp) {
-      const __amdgpu_buffer_rsrc_t rq = make_rsrc(partial_frag(m, sp, rb, nb, a.row_blocks, 8), 8 * 8 * 1024);
+      const __amdgpu_buffer_rsrc_t rq = make_rsrc(partial_frag(m, sp, rb, nb, a.row_blocks, RT), RT * 8 * 1024);
       u32x4 v[4][4];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
@@ -1561,25 +1579,47 @@ void linear_tile_kernel(const LinearArgs a) {
     }
   }
 
-  // epilogue: the 128 rows in two passes of 64 through LDS; in each pass
-  // wave w finishes rows 16w .. 16w + 15 of the pass
+  // epilogue: the R rows in passes of PR through LDS (the rows of a pass
+  // come from the waves whose 64-row half holds them); in each pass wave w
+  // finishes rows 16w .. 16w + 15 of the pass
 #pragma unroll
-  for (int pass = 0; pass < 2; ++pass) {
-    const int prow = row_base + 64 * pass;
+  for (int pass = 0; pass < R / PR; ++pass) {
+    const int prow = row_base + PR * pass;
     if (prow >= M) break;                                  // uniform
     __syncthreads();
-    if (wr == pass) {
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
+    for (int mt = 0; mt < 4; ++mt) {
+      const int tr = 64 * wr + 16 * mt - PR * pass;        // the tile's first row in the pass
+      if (tr >= 0 && tr < PR) {                            // uniform
 #pragma unroll
         for (int i2 = 0; i2 < 4; ++i2)
 #pragma unroll
-          for (int q = 0; q < 4; ++q) zbuf[(16 * mt + 4 * g + q) * 132 + 16 * (4 * wc + i2) + c] = z[mt][i2][q];
+          for (int q = 0; q < 4; ++q) zbuf[(tr + 4 * g + q) * 132 + 16 * (4 * wc + i2) + c] = z[mt][i2][q];
+      }
     }
     __syncthreads();
     if (prow + 16 * wave < M)
       epilogue_rows_lds<4>(zbuf + 16 * wave * 132, 132, ec, lane, m, col0, prow + 16 * wave, M);
   }
+}
+
+// Exchanged (one split per workgroup, about 165 VGPRs): three workgroups per
+// CU, so that the down projection's 640 workgroups at 49-128 rows run in one
+// round instead of 1.25 (-5 to -9 %); chained (about 230 VGPRs): two.
+template <int BITS, bool CHAINED>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(CHAINED ? 2 : 3, CHAINED ? 2 : 3)))
+void linear_tile_kernel(const LinearArgs a) {
+  tile_body<BITS, CHAINED, 2>(a);
+}
+
+// The same exchanged tiling in 64-row tiles of 2 waves (64 x 64 each): with
+// the split-fold launch, the down projection's 40 blocks x 16 splits are 640
+// tiles at up to 64 rows and 1280 at 65-128, 2.5 and 5 per CU, where the
+// 128-row tiles left 128 CUs with three workgroups and 128 with two.
+template <int BITS>
+__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(3, 3)))
+void linear_tile64_kernel(const LinearArgs a) {
+  tile_body<BITS, false, 1>(a);
 }
 
 // ------------------------------------------------------------ linear, 128 x 256 tiles
@@ -2417,6 +2457,7 @@ LinearFn pick_linear(int kernel, bool chained, int rows) {
   if (kernel == kWide128) return linear_wide_kernel<BITS>;
   if (kernel == kBlock128) return chained ? linear_block_kernel<BITS, true> : linear_block_kernel<BITS, false>;
   if (kernel == kBlock64) return linear_block64_kernel<BITS>;
+  if (kernel == kTile64) return linear_tile64_kernel<BITS>;
   if (kernel == kQuad128) return linear_quad_kernel<BITS>;
   return chained ? pick_kernel<BITS, true>(kernel, rows) : pick_kernel<BITS, false>(kernel, rows);
 }
@@ -2437,6 +2478,7 @@ inline void linear_form_name(char *buf, size_t n, int bits, int kernel, bool cha
     case kWide128: snprintf(buf, n, "linear_wide_kernel<%d>", bits); return;
     case kBlock128: snprintf(buf, n, "linear_block_kernel<%d, %s>", bits, ch); return;
     case kBlock64: snprintf(buf, n, "linear_block64_kernel<%d>", bits); return;
+    case kTile64: snprintf(buf, n, "linear_tile64_kernel<%d>", bits); return;
     case kQuad128: snprintf(buf, n, "linear_quad_kernel<%d>", bits); return;
     case kChain16: snprintf(buf, n, "linear_chain_kernel<%d, 1, %s, 4, 8, %d>", bits, ch, pol); return;
     case kChain32: snprintf(buf, n, "linear_chain_kernel<%d, 2, %s, 4, 8, %d>", bits, ch, pol); return;

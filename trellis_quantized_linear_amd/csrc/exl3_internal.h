@@ -47,6 +47,7 @@ struct LinearArgs {
   int32_t xr_chunk_major;     // 128-row tilings: Xr is chunk-major (else row-major)
   int32_t fold_launch;        // 128-row exchanged tiles: store the split partials only; a split-fold
                               // launch adds them and finishes the rows
+  int32_t fold_tiles;         // split-fold launch: 16-row tiles per row block of the partials (8 or 4)
   // Fused input rotation (decode and 32-row launches): the launch itself
   // writes every member's Xr from x before its chains read it. sync[0]
   // counts finished workgroups; sync[1 + j * K/128 + k] says that member j's
@@ -59,10 +60,11 @@ struct LinearArgs {
 };
 
 // Workgroups (one wave each) of the split-fold launch: one per (member, row
-// block, block, 16-row tile, group of 4 rows).
+// block, block, 16-row tile, group of 4 rows); fold_tiles 16-row tiles per
+// row block (8 for 128-row partials, 4 for 64-row ones).
 inline int64_t split_fold_wgs(const LinearArgs &a) {
   int64_t n = 0;
-  for (int j = 0; j < a.n_members; ++j) n += (int64_t)a.row_blocks * a.m[j].n_blocks * 32;
+  for (int j = 0; j < a.n_members; ++j) n += (int64_t)a.row_blocks * a.m[j].n_blocks * a.fold_tiles * 4;
   return n;
 }
 
@@ -113,10 +115,11 @@ enum LinearKernel {
   kQuad128 = 8,     // opt-in single-chain prompt tiles: 128 rows x 4 blocks, 4 waves of 128 x 128
   kChain16H = 9,    // 16 rows, 8 waves, exchanged: two waves per split, 4 column tiles each
   kBlock64 = 10,    // 64 rows x 1 block per workgroup, 4 waves of 64 x 32 (chained, one row block)
+  kTile64 = 11,     // 64 rows per workgroup, 2 waves of 64 x 64 (exchanged, with the split-fold launch)
 };
 
 inline int waves_per_wg(int kernel) {
-  return kernel == kSpread16 ? 16 : (kernel == kChain16x8 || kernel == kChain16H) ? 8 : kWaves;
+  return kernel == kSpread16 ? 16 : (kernel == kChain16x8 || kernel == kChain16H) ? 8 : kernel == kTile64 ? 2 : kWaves;
 }
 inline int threads_per_wg(int kernel) { return 64 * waves_per_wg(kernel); }
 

@@ -59,10 +59,11 @@ __global__ __launch_bounds__(kThreads) void rot_kernel(const RotArgs a) {
 
 // ------------------------------------------------------------ split fold
 //
-// After a 128-row exchanged launch that only stored its split partials
-// (LinearArgs::fold_launch), and for the left blocks of the chained block
-// tiling: one wave per (member, row block, block, 16-row tile, group of 4
-// rows) adds those rows' S partials in split order, z = P0, then z + P1,
+// After a 128- or 64-row exchanged launch that only stored its split
+// partials (LinearArgs::fold_launch; fold_tiles 16-row tiles per row block),
+// and for the left blocks of the chained block tiling: one wave per
+// (member, row block, block, 16-row tile, group of 4 rows) adds those rows'
+// S partials in split order, z = P0, then z + P1,
 // ... (the same fp32 additions, in the same order, as a linear launch's
 // last arriving workgroup would make), and runs the epilogue of its 4
 // rows. A 16-row tile is 512 fragments of 4 rows x 1 column, 8 KB per split
@@ -76,16 +77,17 @@ __global__ __launch_bounds__(64) void split_fold_kernel(const LinearArgs a) {
   const int RB = a.row_blocks;
   int64_t local = blockIdx.x;
   int j = 0;
-  while (j + 1 < a.n_members && local >= (int64_t)RB * a.m[j].n_blocks * 32) {
-    local -= (int64_t)RB * a.m[j].n_blocks * 32;
+  const int TPB = a.fold_tiles;                            // 16-row tiles per row block
+  while (j + 1 < a.n_members && local >= (int64_t)RB * a.m[j].n_blocks * TPB * 4) {
+    local -= (int64_t)RB * a.m[j].n_blocks * TPB * 4;
     ++j;
   }
   const MemberArgs &m = a.m[j];
-  const int per_rb = m.n_blocks * 32;
+  const int per_rb = m.n_blocks * TPB * 4;
   const int rb = (int)(local / per_rb);
   const int rem = (int)(local - (int64_t)rb * per_rb);
-  const int nb = rem >> 5, mt = (rem >> 2) & 7, q = rem & 3;
-  const int row0 = 128 * rb + 16 * mt + 4 * q;
+  const int nb = rem / (TPB * 4), mt = (rem >> 2) % TPB, q = rem & 3;
+  const int row0 = 16 * TPB * rb + 16 * mt + 4 * q;
   if (row0 >= a.M) return;                                 // uniform
   const int S = m.splits;
   const int lane = threadIdx.x;
@@ -96,7 +98,7 @@ __global__ __launch_bounds__(64) void split_fold_kernel(const LinearArgs a) {
 #pragma unroll
   for (int s = 0; s < kMaxSplits; ++s) {
     if (s < S) {                                           // uniform
-      const __amdgpu_buffer_rsrc_t rp = make_rsrc(partial_frag(m, s, rb, nb, RB, 8) + mt * 8 * 256, 8 * 1024);
+      const __amdgpu_buffer_rsrc_t rp = make_rsrc(partial_frag(m, s, rb, nb, RB, TPB) + mt * 8 * 256, 8 * 1024);
 #pragma unroll
       for (int e = 0; e < 2; ++e)
         v[s][e] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
@@ -172,10 +174,10 @@ __global__ void fill_zero_kernel(uint32_t *p, int64_t n) {
 }  // namespace
 
 int launch_linear(const LinearArgs &a, int bits, int kernel, bool chained, void *stream) {
-  if (kernel < kChain16 || kernel > kBlock64 ||
+  if (kernel < kChain16 || kernel > kTile64 ||
       ((kernel == kChain16x8 || kernel == kSpread16 || kernel == kWide128 || kernel == kQuad128 ||
         kernel == kBlock64) && !chained) ||
-      (kernel == kChain16H && chained))
+      ((kernel == kChain16H || kernel == kTile64) && chained))
     return (int)hipErrorInvalidValue;
   switch (bits) {
     case 2: return launch_linear_bits<2>(a, kernel, chained, stream);
@@ -215,6 +217,7 @@ int launch_rot(const RotArgs &a_in, void *stream) {
 }
 
 int launch_split_fold(const LinearArgs &a, void *stream) {
+  if (a.fold_tiles != 4 && a.fold_tiles != 8) return (int)hipErrorInvalidValue;
   const int64_t wgs = split_fold_wgs(a);
   for (int j = 0; j < a.n_members; ++j)
     if (a.m[j].splits < 1 || a.m[j].splits > 16) return (int)hipErrorInvalidValue;
