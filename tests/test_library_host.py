@@ -442,9 +442,9 @@ def test_static_entry_checks_and_mock_launches(lib):
 
 
 def test_split_fold_launch_after_the_exchanged_128_row_tiling(lib):
-    """The down projection (K 17408, N 5120, 16 splits) at 49-128 rows runs the
+    """The down projection (K 17408, N 5120, 16 splits) at 33-128 rows runs the
     exchanged 2 x 2 tiling in 64-row tiles and a split-fold launch after it
-    (three launches with the rotation); at 48 rows the exchanged 16-row form
+    (three launches with the rotation); at 32 rows the exchanged 32-row form
     (two); a forced plan of more than 16 splits keeps the 128-row tiling and
     its own last-arriver fold."""
     ex.exl3_test_mock(True)
@@ -458,9 +458,9 @@ def test_split_fold_launch_after_the_exchanged_128_row_tiling(lib):
                                None) == ex.EXL3_OK
         return ex.exl3_test_mock_counts()[0], ex.exl3_test_last_form()
 
-    for M in (49, 64, 96, 97, 100, 128):
+    for M in (33, 48, 49, 64, 96, 97, 100, 128):
         assert call(M) == (3, "linear_tile64_kernel<4>")
-    assert call(48)[0] == 2
+    assert call(32) == (2, "linear_chain_kernel<4, 2, false, 4, 8, 2>")
     ex.exl3_test_force(-1, -1, 17)
     need17, cb17 = ex.exl3_workspace_need([w], 128)
     ws = ex.exl3_workspace_t(0x200000000, need17, cb17)

@@ -172,11 +172,12 @@ MidChoice mid_m_choice(int64_t blocks, bool long_chains, int64_t M) {
   if (blocks >= 128) return w16 <= 1024 ? MidChoice{1, true} : MidChoice{8, true};
   if (!long_chains) return M <= 32 ? MidChoice{1, false} : MidChoice{1, true};
   // few blocks, long splits (down): the exchange keeps the CUs busy; from
-  // 49 rows on the 128-row exchanged tiles with the split-fold launch (down
-  // at 49, 64, 80 and 96 rows 41-44 us against 45-53 us for the chained
-  // 16-row form)
+  // 33 rows on the exchanged 2 x 2 tiles with the split-fold launch (down at
+  // 49, 64, 80 and 96 rows 41-44 us against 45-53 us for the chained 16-row
+  // form; in 64-row tiles, the MLP at 33 / 48 rows 99-103 -> 93-97 us
+  // against the exchanged 16-row form over three row blocks; at 17-32 rows
+  // the 32-row exchanged form stays, 0.5-3 us faster)
   if (M <= 32) return {2, false};
-  if (M <= 48) return {1, false};
   return {8, false};
 }
 
