@@ -41,12 +41,14 @@ FORMS = {
     # the spread launch: one 16-wave workgroup per CU, spare waves on the left blocks
     "linear_spread_kernel<{b}>": (4, [(256, [34816], 1, ""), (256, [17408, 17408], 16, "")]),
     "linear_spread_kernel<{b}> +rot": (4, [(256, [34816], 7, "rot")]),
-    "linear_spread_rows_kernel<{b}>": (4, [(256, [34816], 17, ""), (256, [17408, 17408], 32, "")]),
+    "linear_spread_rows_kernel<{b}>": (4, [(256, [34816], 17, ""), (256, [17408, 17408], 32, ""), (256, [24576], 48, "")]),
     # 128-row tilings
     "linear_block_kernel<{b}, true>": (2, [(256, [34816], 65, ""), (256, [17408, 17408], 100, ""), (128, [128], 129, ""),
                                           (256, [384], 300, ""), (256, [1024, 256, 256], 200, "")]),
     # 64-row block tiling: a few more blocks than CUs at 33-64 rows (left blocks as single splits)
     "linear_block64_kernel<{b}>": (2, [(256, [34816], 33, ""), (256, [17408, 17408], 64, "")]),
+    # 32-row block tiling: chained block tiles at 17-32 rows (many blocks: the head)
+    "linear_block32_kernel<{b}>": (2, [(128, [248320], 17, ""), (256, [131072], 32, ""), (128, [65536, 65536], 24, "")]),
     # exchanged 2 x 2 tiles of 64 rows (2 waves), partials added by the split-fold launch; the
     # 128-row form (4 waves) is reached only through exl3_test_force now
     "linear_tile64_kernel<{b}>": (3, [(16384, [128], 97, ""), (16384, [128, 256], 64, ""), (17408, [5120], 49, ""),

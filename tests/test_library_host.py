@@ -343,7 +343,7 @@ def test_rotation_runs_inside_the_linear_launch_up_to_32_rows(lib):
         ex.exl3_test_force(-1, -1, 0)
         # the {gate, up} pair: one launch at 16 rows (spread launch, one row
         # block); at 17-32 rows the spread launch covers several row blocks
-        # and keeps its rotation launch; at 33 and 48 rows the 128-row block
+        # and keeps its rotation launch; at 33 and 48 rows the 64-row block
         # tiling with its left blocks (rotation, tiling, split fold)
         g = fake_weight(5120, 17408, 4, base=0x60000000)
         u = fake_weight(5120, 17408, 4, base=0x70000000)

@@ -142,7 +142,8 @@ constexpr int64_t kSpreadMaxRows = 48;
 // chained block tiling with its left blocks (at 33, 40 and 48 rows 70-74 us
 // on 128-row workgroups, split-fold launch included, against 73-79 us over
 // three 16-row blocks; 64-row workgroups since, below); the same bits
-// either way.
+// either way. At 17-32 rows the spread launch stays faster than the 32-row
+// block tiling with left blocks (the MLP 88-89 against 90-93 us).
 constexpr int64_t kSpreadMaxRowsLeft = 32;
 
 // The chained 128-row block tiling can give the blocks past one per CU to
@@ -292,10 +293,12 @@ Launch choose_launch(const MemberPlan *mp, int n, int64_t M) {
   // Automatic chained 128-row block tiles of at most 64 rows run 64-row
   // workgroups: half the MFMAs, the same bits (3-bit {gate, up} pair: MLP at
   // 33-64 rows 112-129 -> 98-116 us; 6-bit head at 49 / 64 rows 406-411 /
-  // 384-394 -> 358-361 / 328-345 us)
+  // 384-394 -> 358-361 / 328-345 us); of at most 32 rows 32-row workgroups
+  // (the 6-bit head at 17 / 24 / 32 rows 329-336 / 301 / 290-294 ->
+  // 297-303 / 275-278 / 263-269 us)
   if (L.kernel == exl3::kBlock128 && L.chained && M <= 64 && g_hooks.m_tiles == -1) {
-    L.kernel = exl3::kBlock64;
-    L.m_tiles = 4;
+    L.kernel = M <= 32 ? exl3::kBlock32 : exl3::kBlock64;
+    L.m_tiles = M <= 32 ? 2 : 4;
   }
   L.exchange = !L.chained || (spread && L.left_blocks > 0);
   // The 2 x 2 tiling's exchange adds 64 KB partials: its last arriving
@@ -321,7 +324,8 @@ Launch choose_launch(const MemberPlan *mp, int n, int64_t M) {
   // set the launch time; instead each CU's workgroup runs one split of one
   // of them after its own block, and the split-fold launch adds those
   // partials.
-  if ((L.kernel == exl3::kBlock128 || L.kernel == exl3::kBlock64) && L.chained && L.row_blocks == 1 && left_fits) {
+  if ((L.kernel == exl3::kBlock128 || L.kernel == exl3::kBlock64 || L.kernel == exl3::kBlock32) && L.chained &&
+      L.row_blocks == 1 && left_fits) {
     L.block_left = true;
     L.own_blocks = ncu;
     L.left_blocks = blocks - ncu;
@@ -587,7 +591,8 @@ int run_group(int32_t n_members, const exl3_weight_t *const *w, const void *x, i
   // Chunk offsets are 32-bit: chunk-major needs 2 K M < 2^31, which every
   // accepted call meets (check_group).
   const bool tile_cm = (L.kernel == exl3::kTile128 || L.kernel == exl3::kBlock128 || L.kernel == exl3::kWide128 ||
-                        L.kernel == exl3::kQuad128 || L.kernel == exl3::kBlock64 || L.kernel == exl3::kTile64) &&
+                        L.kernel == exl3::kQuad128 || L.kernel == exl3::kBlock64 || L.kernel == exl3::kTile64 ||
+                        L.kernel == exl3::kBlock32) &&
                        2 * K * M < (int64_t(1) << 31);
   // The 16-row column-halves launch ({q, k, v} at decode rows) reads its
   // 16 rows of a chunk as 8 whole lines instead of 16 half-used ones (the

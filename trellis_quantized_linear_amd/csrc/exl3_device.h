@@ -1904,7 +1904,8 @@ void linear_wide_kernel(const LinearArgs a) {
 // of column tiles 2w, 2w + 1 (8 x 2 MFMA tiles), so each decoded B operand
 // feeds 8 MFMAs, and two workgroups fit on a CU (two waves per SIMD).
 // linear_block64_kernel is the same with 64 rows (4 x 2 MFMA tiles a wave)
-// for launches of at most 64 rows. The operands reach LDS as in the
+// for launches of at most 64 rows, linear_block32_kernel with 32 rows (2 x 2)
+// for launches of at most 32 rows. The operands reach LDS as in the
 // 128 x 256 tiling: buffer-to-LDS copies into a 6-stage ring, input operands
 // stored linearly, tile rows of words in padded slots. Chained: every split of the block, folded in split order (then,
 // with left blocks, one split of a left block, its partial stored for the
@@ -1914,7 +1915,8 @@ void linear_wide_kernel(const LinearArgs a) {
 
 template <int BITS, int RT = 8>
 struct BlockLds {
-  static constexpr int kA = RT * 16 * 64;                    // input tile of one chunk (RT * 16 rows)
+  static constexpr int kAT = RT < 4 ? 4 : RT;                // input operand slots: one copy per wave at least
+  static constexpr int kA = kAT * 16 * 64;                   // input tile of one chunk (RT * 16 rows used)
   static constexpr int kRowBytes = 256 * BITS;               // one tile row (8 tiles) of the block
   static constexpr int kRow = 2048 + 128;                    // its slot: two 1 KB halves (4 tiles each) + 128 bytes
   static constexpr int kStage = kA + 2 * kRow;
@@ -1923,17 +1925,18 @@ struct BlockLds {
   static constexpr int kZ = RT * 16 * 132 * 4;               // epilogue: the block's Z, 132-float rows
   static constexpr int kBytes = kRing > kZ ? kRing : kZ;
   static constexpr int kPiece = kRowBytes / 2;               // bytes of a half tile row (4 tiles, <= 1 KB)
-  static constexpr int kCopies = RT / 4 + 1;                 // copies per wave and chunk: RT / 4 input operands + a piece
+  static constexpr int kCopies = kAT / 4 + 1;                // copies per wave and chunk: kAT / 4 input operands + a piece
 };
 
 // RT row tiles of 16 per workgroup: 8 (128 rows) or, chained, 4 (64 rows,
-// for launches of at most 64 rows: half the MFMAs, the same bits per row).
+// for launches of at most 64 rows: half the MFMAs, the same bits per row)
+// or 2 (32 rows, at most 32).
 template <int BITS, bool CHAINED, int RT>
 __device__ __forceinline__ void block_body(const LinearArgs &a) {
-  static_assert(RT == 8 || (RT == 4 && CHAINED), "64-row workgroups: chained only");
+  static_assert(RT == 8 || ((RT == 4 || RT == 2) && CHAINED), "64- and 32-row workgroups: chained only");
   using BL = BlockLds<BITS, RT>;
   constexpr int R = 16 * RT;                                 // rows per workgroup
-  constexpr int AE = RT / 4;                                 // input operands each wave copies per chunk
+  constexpr int AE = BL::kAT / 4;                            // input operands each wave copies per chunk
   using TR = BitsTraits<BITS>;
   constexpr int NS = BL::kStages;
   constexpr int ND = TR::kDwords;
@@ -1971,7 +1974,9 @@ __device__ __forceinline__ void block_body(const LinearArgs &a) {
 
   // copies: wave w moves input operands AE w + e (lane l brings row
   // 16 (AE w + e) + l % 16, 16-byte column l / 16) and half w % 2 of tile
-  // row w / 2 of every chunk
+  // row w / 2 of every chunk; with 2 row tiles, waves 2 and 3 fill unused
+  // operand slots with zeros (out-of-range copies, no memory read), so every
+  // wave counts the same copies per chunk
   auto xr_rsrc = [&](const MemberArgs &mm) {
     return a.xr_chunk_major ? make_rsrc(mm.xr + (int64_t)row_base * kChunk, (uint32_t)(C * M - row_base) * 64u)
                             : make_rsrc(mm.xr + (int64_t)row_base * K, (uint32_t)min(M - row_base, R) * (uint32_t)K * 2u);
@@ -1984,7 +1989,7 @@ __device__ __forceinline__ void block_body(const LinearArgs &a) {
 #pragma unroll
   for (int e = 0; e < AE; ++e) {
     const int r = 16 * (AE * wave + e) + c;
-    va[e] = row_base + r < M ? (uint32_t)(r * a_row + 16 * g) : kOutOfRange;
+    va[e] = AE * wave + e < RT && row_base + r < M ? (uint32_t)(r * a_row + 16 * g) : kOutOfRange;
   }
   __amdgpu_buffer_rsrc_t rw = make_rsrc(m.words + (int64_t)nb * m.block_stride, (uint32_t)m.block_stride);
   const int hrow = wave >> 1, half = wave & 1;
@@ -2192,9 +2197,9 @@ __device__ __forceinline__ void block_body(const LinearArgs &a) {
   const EpiCols ec = epi_cols(m, col0, lane);
   __syncthreads();
 #pragma unroll
-  for (int i = 0; i < RT / 4; ++i) {
+  for (int i = 0; i < (RT + 3) / 4; ++i) {
     const int r16 = 16 * (wave + 4 * i);
-    if (row_base + r16 < M) epilogue_rows_lds<4>(zb + r16 * 132, 132, ec, lane, m, col0, row_base + r16, M);
+    if (r16 < R && row_base + r16 < M) epilogue_rows_lds<4>(zb + r16 * 132, 132, ec, lane, m, col0, row_base + r16, M);
   }
 
   if constexpr (CHAINED) {
@@ -2246,6 +2251,12 @@ template <int BITS>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void linear_block64_kernel(const LinearArgs a) {
   block_body<BITS, true, 4>(a);
+}
+
+template <int BITS>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void linear_block32_kernel(const LinearArgs a) {
+  block_body<BITS, true, 2>(a);
 }
 
 // ------------------------------------------------------------ linear, opt-in single-chain prompt tiles
@@ -2457,6 +2468,7 @@ LinearFn pick_linear(int kernel, bool chained, int rows) {
   if (kernel == kWide128) return linear_wide_kernel<BITS>;
   if (kernel == kBlock128) return chained ? linear_block_kernel<BITS, true> : linear_block_kernel<BITS, false>;
   if (kernel == kBlock64) return linear_block64_kernel<BITS>;
+  if (kernel == kBlock32) return linear_block32_kernel<BITS>;
   if (kernel == kTile64) return linear_tile64_kernel<BITS>;
   if (kernel == kQuad128) return linear_quad_kernel<BITS>;
   return chained ? pick_kernel<BITS, true>(kernel, rows) : pick_kernel<BITS, false>(kernel, rows);
@@ -2478,6 +2490,7 @@ inline void linear_form_name(char *buf, size_t n, int bits, int kernel, bool cha
     case kWide128: snprintf(buf, n, "linear_wide_kernel<%d>", bits); return;
     case kBlock128: snprintf(buf, n, "linear_block_kernel<%d, %s>", bits, ch); return;
     case kBlock64: snprintf(buf, n, "linear_block64_kernel<%d>", bits); return;
+    case kBlock32: snprintf(buf, n, "linear_block32_kernel<%d>", bits); return;
     case kTile64: snprintf(buf, n, "linear_tile64_kernel<%d>", bits); return;
     case kQuad128: snprintf(buf, n, "linear_quad_kernel<%d>", bits); return;
     case kChain16: snprintf(buf, n, "linear_chain_kernel<%d, 1, %s, 4, 8, %d>", bits, ch, pol); return;

@@ -116,6 +116,7 @@ enum LinearKernel {
   kChain16H = 9,    // 16 rows, 8 waves, exchanged: two waves per split, 4 column tiles each
   kBlock64 = 10,    // 64 rows x 1 block per workgroup, 4 waves of 64 x 32 (chained, one row block)
   kTile64 = 11,     // 64 rows per workgroup, 2 waves of 64 x 64 (exchanged, with the split-fold launch)
+  kBlock32 = 12,    // 32 rows x 1 block per workgroup, 4 waves of 32 x 32 (chained, one row block)
 };
 
 inline int waves_per_wg(int kernel) {

@@ -174,9 +174,9 @@ __global__ void fill_zero_kernel(uint32_t *p, int64_t n) {
 }  // namespace
 
 int launch_linear(const LinearArgs &a, int bits, int kernel, bool chained, void *stream) {
-  if (kernel < kChain16 || kernel > kTile64 ||
+  if (kernel < kChain16 || kernel > kBlock32 ||
       ((kernel == kChain16x8 || kernel == kSpread16 || kernel == kWide128 || kernel == kQuad128 ||
-        kernel == kBlock64) && !chained) ||
+        kernel == kBlock64 || kernel == kBlock32) && !chained) ||
       ((kernel == kChain16H || kernel == kTile64) && chained))
     return (int)hipErrorInvalidValue;
   switch (bits) {
